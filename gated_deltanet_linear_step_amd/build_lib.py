@@ -1,0 +1,37 @@
+"""Build libgdn.so (all HIP kernels + the C ABI) for gfx950, in-tree.
+
+    python -m gated_deltanet_linear_step_amd.build_lib
+
+hipcc cross-compiles for gfx950 without a GPU. Packed-FP32 instructions are
+disabled for the device code (``-packed-fp32-ops``).
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgdn.so")
+SOURCES = ["gdn_api.cpp", "gdn_conv.hip", "gdn_decode.hip", "gdn_prefill.hip"]
+ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-command-line-argument",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-x", "hip"] + srcs + ["-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

@@ -1,0 +1,276 @@
+// gdn_api.cpp -- the C ABI of libgdn.so (declared in include/gdn.h).
+//
+// Every entry point validates all of its arguments on the host before the first
+// HIP call, so a call that returns an error has launched nothing and changed
+// no buffer. Only GDN_ERR_LAUNCH is reported after a launch was attempted.
+
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "gdn_kernels.h"
+
+namespace {
+
+constexpr uint32_t kKnownFlags = GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM;
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+bool dtype_ok(int32_t dt) { return dt == GDN_F32 || dt == GDN_F16 || dt == GDN_BF16; }
+int64_t dtype_size(int32_t dt) { return dt == GDN_F32 ? 4 : 2; }
+
+bool aligned(const void *p, int64_t bytes)
+{
+    return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(bytes)) == 0;
+}
+
+// Checks shared by the decode step and the prefill: dims, flags and the inputs
+// the flags require. On success fills the kernel-side copies.
+gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dtype,
+                        const void *out, const float *state, bool (*supported)(int, int),
+                        gdn::HeadCfg &hc, gdn::ActInputs &ai)
+{
+    if (!d || !in || !out || !state)
+        return GDN_ERR_NULL;
+    if (d->num_k_heads < 1 || d->num_v_heads < 1 || d->num_v_heads % d->num_k_heads != 0)
+        return GDN_ERR_SHAPE;
+    if (d->head_dim_k < 1 || d->head_dim_v < 1)
+        return GDN_ERR_SHAPE;
+    if (d->head_map != GDN_MAP_GROUPED && d->head_map != GDN_MAP_TILED)
+        return GDN_ERR_SHAPE;
+    if ((d->flags & ~kKnownFlags) != 0)
+        return GDN_ERR_UNSUPPORTED;
+    if (!supported(d->head_dim_k, d->head_dim_v))
+        return GDN_ERR_UNSUPPORTED;
+    if (!(std::isfinite(d->scale) && std::isfinite(d->l2_eps) && std::isfinite(d->norm_eps)) ||
+        d->scale < 0.f || d->l2_eps < 0.f || d->norm_eps < 0.f)
+        return GDN_ERR_SHAPE;
+    if (!dtype_ok(out_dtype) || !dtype_ok(in->qkv_dtype))
+        return GDN_ERR_UNSUPPORTED;
+    if (!in->q || !in->k || !in->v)
+        return GDN_ERR_NULL;
+    const int64_t qk_w = (int64_t)d->num_k_heads * d->head_dim_k;
+    const int64_t v_w = (int64_t)d->num_v_heads * d->head_dim_v;
+    if (in->q_stride < qk_w || in->k_stride < qk_w || in->v_stride < v_w)
+        return GDN_ERR_SHAPE;
+    // q and k are read as groups of 4 elements: base and row stride must keep
+    // every group aligned to 4 elements.
+    const int64_t es = dtype_size(in->qkv_dtype);
+    if (!aligned(in->q, 4 * es) || !aligned(in->k, 4 * es) || !aligned(in->v, es) ||
+        in->q_stride % 4 != 0 || in->k_stride % 4 != 0)
+        return GDN_ERR_ALIGN;
+    if (d->flags & GDN_RAW_GATES) {
+        if (!in->a || !in->b || !in->decay_param || !in->dt_bias)
+            return GDN_ERR_NULL;
+        if (!dtype_ok(in->ab_dtype))
+            return GDN_ERR_UNSUPPORTED;
+        if (d->decay != GDN_DECAY_LOG_RATE && d->decay != GDN_DECAY_NEGATIVE_RATE)
+            return GDN_ERR_SHAPE;
+    } else if (!in->g || !in->beta) {
+        return GDN_ERR_NULL;
+    }
+    if (d->flags & GDN_GATED_NORM) {
+        if (!in->z || !in->norm_weight)
+            return GDN_ERR_NULL;
+        if (!dtype_ok(in->z_dtype))
+            return GDN_ERR_UNSUPPORTED;
+    }
+    if (!aligned(state, 16))
+        return GDN_ERR_ALIGN;
+
+    hc.Hk = d->num_k_heads;
+    hc.Hv = d->num_v_heads;
+    hc.dk = d->head_dim_k;
+    hc.dv = d->head_dim_v;
+    hc.head_map = d->head_map;
+    hc.decay_kind = d->decay;
+    hc.flags = d->flags;
+    hc.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim_k);
+    hc.l2_eps = d->l2_eps > 0.f ? d->l2_eps : 1e-6f;
+    hc.norm_eps = d->norm_eps > 0.f ? d->norm_eps : 1e-6f;
+
+    ai.q = in->q;
+    ai.k = in->k;
+    ai.v = in->v;
+    ai.q_stride = in->q_stride;
+    ai.k_stride = in->k_stride;
+    ai.v_stride = in->v_stride;
+    ai.qkv_dt = in->qkv_dtype;
+    ai.a = in->a;
+    ai.b = in->b;
+    ai.ab_dt = in->ab_dtype;
+    ai.decay_param = in->decay_param;
+    ai.dt_bias = in->dt_bias;
+    ai.g = in->g;
+    ai.beta = in->beta;
+    ai.z = in->z;
+    ai.z_dt = in->z_dtype;
+    ai.norm_w = in->norm_weight;
+    return GDN_OK;
+}
+
+gdn_status launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+// Validates host cu_seqlens; fills the chunk counts the prefill grid needs.
+gdn_status check_cu(const int32_t *cu, int32_t n, int32_t total, int64_t *chunks, int64_t *max_chunks)
+{
+    if (cu[0] != 0 || cu[n] != total)
+        return GDN_ERR_SHAPE;
+    int64_t c = 0, mx = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (cu[i + 1] < cu[i])
+            return GDN_ERR_SHAPE;
+        const int64_t ci = ((int64_t)cu[i + 1] - cu[i] + gdn::kChunk - 1) / gdn::kChunk;
+        c += ci;
+        if (ci > mx)
+            mx = ci;
+    }
+    *chunks = c;
+    *max_chunks = mx;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status s)
+{
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "inconsistent sizes or sequence offsets";
+    case GDN_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case GDN_ERR_OVERFLOW: return "an element count or offset exceeds the kernels' index range";
+    case GDN_ERR_ALIGN: return "a pointer or stride is not aligned as required";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+    }
+    return "unknown status";
+}
+
+int32_t gdn_version(void) { return 100; }
+
+gdn_status gdn_conv_update(int32_t channels, int32_t kernel_size, int32_t num_seqs,
+                           const int32_t *cu_seqlens, int32_t total_tokens, int32_t x_dtype,
+                           const void *x, int64_t x_stride, const void *weight, void *conv_state,
+                           int32_t y_dtype, void *y, int64_t y_stride, void *stream)
+{
+    if (channels < 1 || num_seqs < 0 || total_tokens < 0)
+        return GDN_ERR_SHAPE;
+    if (kernel_size < 2 || kernel_size > 8)
+        return GDN_ERR_UNSUPPORTED;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype))
+        return GDN_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && num_seqs == 0)
+        return GDN_ERR_SHAPE;
+    if (num_seqs == 0 || total_tokens == 0)
+        return GDN_OK;  // nothing to do; states untouched
+    if (!x || !weight || !conv_state || !y)
+        return GDN_ERR_NULL;
+    if (x_stride < channels || y_stride < channels)
+        return GDN_ERR_SHAPE;
+    if (!cu_seqlens && total_tokens % num_seqs != 0)
+        return GDN_ERR_SHAPE;
+    const int64_t cblocks = ((int64_t)channels + 255) / 256;
+    if (cblocks * total_tokens > kI32Max)
+        return GDN_ERR_OVERFLOW;
+    gdn::ConvParams p{};
+    p.C = channels;
+    p.K = kernel_size;
+    p.N = num_seqs;
+    p.total = total_tokens;
+    p.uniform_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    p.cu = cu_seqlens;
+    p.x = x;
+    p.x_stride = x_stride;
+    p.w = weight;
+    p.state = conv_state;
+    p.y = y;
+    p.y_stride = y_stride;
+    p.x_dt = x_dtype;
+    p.y_dt = y_dtype;
+    return launch_status(gdn::launch_conv(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
+                           const gdn_inputs *in, float *state, const int32_t *state_slots,
+                           int32_t num_slots, int32_t out_dtype, void *out, void *stream)
+{
+    gdn::DecodeParams p{};
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::decode_supported, p.hc, p.in);
+    if (st != GDN_OK)
+        return st;
+    if (batch < 0 || tokens_per_seq < 1 || num_slots < 0)
+        return GDN_ERR_SHAPE;
+    if (!state_slots && num_slots < batch)
+        return GDN_ERR_SHAPE;
+    if ((int64_t)batch * tokens_per_seq > kI32Max || (int64_t)batch * dims->num_v_heads > kI32Max)
+        return GDN_ERR_OVERFLOW;
+    if (batch == 0)
+        return GDN_OK;
+    p.state = state;
+    p.slots = state_slots;
+    p.num_slots = num_slots;
+    p.out = out;
+    p.out_dt = out_dtype;
+    p.B = batch;
+    p.T = tokens_per_seq;
+    return launch_status(gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_dims *d, int32_t num_seqs, int32_t total_tokens)
+{
+    if (!d || num_seqs < 0 || total_tokens < 0 || d->num_k_heads < 1 || d->num_v_heads < 1 ||
+        d->num_v_heads % d->num_k_heads != 0 || !gdn::prefill_supported(d->head_dim_k, d->head_dim_v))
+        return 0;
+    const int64_t max_chunks = (int64_t)total_tokens / gdn::kChunk + num_seqs;
+    return gdn::prefill_workspace_bytes(d->num_k_heads, d->num_v_heads, d->head_dim_k,
+                                        d->head_dim_v, max_chunks, num_seqs);
+}
+
+gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
+                               const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                               int32_t total_tokens, const gdn_inputs *in, float *state,
+                               int32_t out_dtype, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    gdn::PrefillParams p{};
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::prefill_supported, p.hc, p.in);
+    if (st != GDN_OK)
+        return st;
+    if (num_seqs < 0 || total_tokens < 0)
+        return GDN_ERR_SHAPE;
+    if (!cu_seqlens_host || !cu_seqlens_dev)
+        return GDN_ERR_NULL;
+    if (num_seqs == 0)
+        return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    int64_t chunks = 0, max_chunks = 0;
+    st = check_cu(cu_seqlens_host, num_seqs, total_tokens, &chunks, &max_chunks);
+    if (st != GDN_OK)
+        return st;
+    if ((int64_t)total_tokens * dims->num_v_heads > kI32Max || chunks * dims->num_v_heads > kI32Max)
+        return GDN_ERR_OVERFLOW;
+    const size_t need = gdn_prefill_workspace_bytes(dims, num_seqs, total_tokens);
+    if (!workspace || workspace_bytes < need)
+        return GDN_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return GDN_ERR_ALIGN;
+    if (total_tokens == 0)
+        return GDN_OK;  // every sequence empty: states untouched
+    p.state = state;
+    p.out = out;
+    p.out_dt = out_dtype;
+    p.N = num_seqs;
+    p.total = total_tokens;
+    p.cu = cu_seqlens_dev;
+    p.num_chunks = (int)chunks;
+    p.max_seq_chunks = (int)max_chunks;
+    gdn::prefill_carve(p, workspace, (int64_t)total_tokens / gdn::kChunk + num_seqs);
+    return launch_status(gdn::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// gdn_kernels.h -- kernel parameter blocks and launchers (host side of the kernels).
+// The C ABI layer (gdn_api.cpp) validates arguments, fills these blocks and
+// calls the launchers; each launcher returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct ActInputs {
+    const void *q, *k, *v;
+    int64_t q_stride, k_stride, v_stride;
+    int qkv_dt;
+    const void *a, *b;
+    int ab_dt;
+    const float *decay_param, *dt_bias;
+    const float *g, *beta;
+    const void *z;
+    int z_dt;
+    const float *norm_w;
+};
+
+struct HeadCfg {
+    int Hk, Hv, dk, dv, head_map, decay_kind;
+    uint32_t flags;
+    float scale, l2_eps, norm_eps;
+};
+
+struct DecodeParams {
+    ActInputs in;
+    HeadCfg hc;
+    float *state;
+    const int32_t *slots;
+    int num_slots;
+    void *out;
+    int out_dt;
+    int B, T;
+};
+
+struct ConvParams {
+    int C, K, N, total, uniform_len;
+    const int32_t *cu;
+    const void *x;
+    int64_t x_stride;
+    const void *w;
+    void *state;
+    void *y;
+    int64_t y_stride;
+    int x_dt, y_dt;
+};
+
+// Prefill geometry: 64-token chunks that start at each sequence's first token.
+constexpr int kChunk = 64;
+
+struct PrefillParams {
+    ActInputs in;
+    HeadCfg hc;
+    float *state;
+    void *out;
+    int out_dt;
+    int N, total;
+    const int32_t *cu;  // device [N+1]
+    int num_chunks;     // sum over sequences of ceil(len / 64)
+    int max_seq_chunks; // largest per-sequence chunk count
+    // workspace carve-out (device pointers)
+    int32_t *chunk_seq;    // [num_chunks] sequence of each chunk
+    int32_t *chunk_start;  // [num_chunks] first packed token row
+    int32_t *chunk_len;    // [num_chunks] tokens in the chunk (1..64)
+    int32_t *seq_chunk0;   // [N] index of each sequence's first chunk
+    uint16_t *qn;          // [num_chunks][Hk][64][dk]   f16, normalised q rows
+    uint16_t *knT;         // [num_chunks][Hk][dk][64]   f16, normalised k, transposed
+    uint16_t *wmat;        // [num_chunks][Hv][64][dk]   f16, W = T diag(beta*gamma) K
+    float *umat;           // [num_chunks][Hv][64][dv]   f32, U = T diag(beta) V
+    uint16_t *aqk;         // [num_chunks][Hv][64][64]   f16, masked decayed Q K^T
+    float *gam;            // [num_chunks][Hv][64]       f32, gamma_t = exp(G_t)
+};
+
+bool decode_supported(int dk, int dv);
+hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
+hipError_t launch_conv(const ConvParams &p, hipStream_t s);
+bool prefill_supported(int dk, int dv);
+size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N);
+void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks);
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,262 @@
+"""Thin ctypes binding over libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgdn.so. Tensors must already live on the GPU; the current torch
+stream is passed to the library. If the library has not been built, the first
+call raises -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_OK = 0
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+                4: "GDN_ERR_OVERFLOW", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_WORKSPACE",
+                7: "GDN_ERR_LAUNCH"}
+F32, F16, BF16 = 0, 1, 2
+MAP_GROUPED, MAP_TILED = 0, 1
+DECAY_LOG_RATE, DECAY_NEGATIVE_RATE = 0, 1
+L2NORM_QK, RAW_GATES, GATED_NORM = 1, 2, 4
+CHUNK = 64
+
+EXPORTED = ["gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
+            "gdn_prefill_chunked", "gdn_status_string", "gdn_version"]
+
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_VP = ctypes.c_void_p
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("head_map", ctypes.c_int32), ("decay", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("scale", ctypes.c_float),
+                ("l2_eps", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+class Inputs(ctypes.Structure):
+    _fields_ = [("q", _VP), ("k", _VP), ("v", _VP),
+                ("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+                ("v_stride", ctypes.c_int64), ("qkv_dtype", ctypes.c_int32),
+                ("a", _VP), ("b", _VP), ("ab_dtype", ctypes.c_int32),
+                ("decay_param", _VP), ("dt_bias", _VP),
+                ("g", _VP), ("beta", _VP),
+                ("z", _VP), ("z_dtype", ctypes.c_int32), ("norm_weight", _VP)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdn.so from the package directory (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_version.restype = ctypes.c_int32
+    lib.gdn_conv_update.restype = ctypes.c_int
+    lib.gdn_conv_update.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP,
+                                    ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int64, _VP, _VP,
+                                    ctypes.c_int32, _VP, ctypes.c_int64, _VP]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.POINTER(Inputs), _VP, _VP, ctypes.c_int32,
+                                    ctypes.c_int32, _VP, _VP]
+    lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32,
+                                                ctypes.c_int32]
+    lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_chunked.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _VP, _VP,
+                                        ctypes.c_int32, ctypes.POINTER(Inputs), _VP,
+                                        ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != GDN_OK:
+        raise GdnError(status, what)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _row_view(t, width: int, name: str):
+    """(tensor, row stride in elements) for a [rows, ..., width-elements] activation."""
+    if t.dim() < 2:
+        raise ValueError(f"{name}: need at least 2 dims")
+    flat_inner = 1
+    for s in t.shape[1:]:
+        flat_inner *= s
+    if flat_inner != width:
+        raise ValueError(f"{name}: inner size {flat_inner} != {width}")
+    # inner dims must be contiguous; the row stride may be larger (views into a mixed row)
+    exp = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.shape[d] != 1 and t.stride(d) != exp:
+            raise ValueError(f"{name}: inner dims must be contiguous")
+        exp *= t.shape[d]
+    return t, t.stride(0)
+
+
+def make_dims(Hk, Hv, dk, dv, head_map, flags, decay=DECAY_LOG_RATE, scale=0.0, l2_eps=0.0,
+              norm_eps=0.0) -> Dims:
+    return Dims(Hk, Hv, dk, dv, head_map, decay, flags, scale, l2_eps, norm_eps)
+
+
+def make_inputs(q, k, v, *, Hk, Hv, dk, dv, a=None, b=None, decay_param=None, dt_bias=None,
+                g=None, beta=None, z=None, norm_weight=None):
+    q, qs = _row_view(q, Hk * dk, "q")
+    k, ks = _row_view(k, Hk * dk, "k")
+    v, vs = _row_view(v, Hv * dv, "v")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    keep = [q, k, v]
+    inp = Inputs(q=_ptr(q), k=_ptr(k), v=_ptr(v), q_stride=qs, k_stride=ks, v_stride=vs,
+                 qkv_dtype=_dt(q))
+    if a is not None:
+        for t in (a, b):
+            if not t.is_contiguous():
+                raise ValueError("a, b must be contiguous [tokens][Hv]")
+        if decay_param.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+            raise TypeError("decay_param and dt_bias must be float32")
+        inp.a, inp.b, inp.ab_dtype = _ptr(a), _ptr(b), _dt(a)
+        inp.decay_param, inp.dt_bias = _ptr(decay_param), _ptr(dt_bias)
+        keep += [a, b, decay_param, dt_bias]
+    if g is not None:
+        if g.dtype != torch.float32 or beta.dtype != torch.float32:
+            raise TypeError("g and beta must be float32")
+        if not (g.is_contiguous() and beta.is_contiguous()):
+            raise ValueError("g, beta must be contiguous [tokens][Hv]")
+        inp.g, inp.beta = _ptr(g), _ptr(beta)
+        keep += [g, beta]
+    if z is not None:
+        if not z.is_contiguous():
+            raise ValueError("z must be contiguous [tokens][Hv][dv]")
+        if norm_weight.dtype != torch.float32:
+            raise TypeError("norm_weight must be float32")
+        inp.z, inp.z_dtype, inp.norm_weight = _ptr(z), _dt(z), _ptr(norm_weight)
+        keep += [z, norm_weight]
+    return inp, keep
+
+
+def conv_update(x, weight, conv_state, *, cu_seqlens=None, num_seqs=None, y=None,
+                y_dtype=torch.float32, stream=None):
+    """Causal depthwise conv + SiLU over x [tokens][C] (rows may be strided),
+    weight [C][K], conv_state [N][C][K-1] (updated in place). Returns y."""
+    total, C = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x channels must be contiguous")
+    K = weight.shape[1]
+    N = conv_state.shape[0] if num_seqs is None else num_seqs
+    if weight.dtype != x.dtype or conv_state.dtype != x.dtype:
+        raise TypeError("weight and conv_state must have x's dtype")
+    if not (weight.is_contiguous() and conv_state.is_contiguous()):
+        raise ValueError("weight and conv_state must be contiguous")
+    if y is None:
+        y = torch.empty((total, C), dtype=y_dtype, device=x.device)
+    st = load().gdn_conv_update(C, K, N, _ptr(cu_seqlens), total, _dt(x), _ptr(x), x.stride(0),
+                                _ptr(weight), _ptr(conv_state), _dt(y), _ptr(y), y.stride(0),
+                                _stream(stream))
+    _check(st, "gdn_conv_update")
+    return y
+
+
+def decode_step(q, k, v, state, *, Hk, Hv, dk, dv, head_map, batch, tokens_per_seq=1,
+                a=None, b=None, decay_param=None, dt_bias=None, g=None, beta=None, z=None,
+                norm_weight=None, l2norm_qk=True, decay=DECAY_LOG_RATE, scale=0.0,
+                state_slots=None, out=None, out_dtype=torch.float32, stream=None):
+    """One call of gdn_decode_step. q, k [B*T][Hk*dk] (views allowed), v [B*T][Hv*dv],
+    state [slots][Hv][dv][dk] f32 updated in place. Returns out [B*T][Hv][dv]."""
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be contiguous float32")
+    rows = batch * tokens_per_seq
+    if out is None:
+        out = torch.empty((rows, Hv, dv), dtype=out_dtype, device=state.device)
+    num_slots = state.shape[0]
+    st = load().gdn_decode_step(ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(inp),
+                                _ptr(state), _ptr(state_slots), num_slots, _dt(out), _ptr(out),
+                                _stream(stream))
+    _check(st, "gdn_decode_step")
+    del keep
+    return out
+
+
+def prefill_workspace_bytes(*, Hk, Hv, dk, dv, head_map=MAP_GROUPED, num_seqs, total_tokens):
+    dims = make_dims(Hk, Hv, dk, dv, head_map, 0)
+    return int(load().gdn_prefill_workspace_bytes(ctypes.byref(dims), num_seqs, total_tokens))
+
+
+def prefill_chunked(q, k, v, state, cu_seqlens, *, Hk, Hv, dk, dv, head_map, a=None, b=None,
+                    decay_param=None, dt_bias=None, g=None, beta=None, z=None, norm_weight=None,
+                    l2norm_qk=True, decay=DECAY_LOG_RATE, scale=0.0, out=None,
+                    out_dtype=torch.float32, workspace=None, cu_seqlens_host=None, stream=None):
+    """One call of gdn_prefill_chunked over packed sequences (cu_seqlens int32 [N+1]).
+    state [N][Hv][dv][dk] f32: initial in, final out. Returns out [tokens][Hv][dv]."""
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.to("cpu", torch.int32).contiguous()
+    cu_dev = cu_seqlens if cu_seqlens.is_cuda else cu_seqlens.to(state.device)
+    N = cu_seqlens_host.numel() - 1
+    total = int(cu_seqlens_host[-1])
+    if out is None:
+        out = torch.empty((total, Hv, dv), dtype=out_dtype, device=state.device)
+    need = load().gdn_prefill_workspace_bytes(ctypes.byref(dims), N, total)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=state.device)
+    host_ptr = ctypes.c_void_p(cu_seqlens_host.data_ptr())
+    st = load().gdn_prefill_chunked(ctypes.byref(dims), N, host_ptr, _ptr(cu_dev), total,
+                                    ctypes.byref(inp), _ptr(state), _dt(out), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "gdn_prefill_chunked")
+    del keep
+    return out

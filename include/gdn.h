@@ -1,0 +1,212 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta-rule library, libgdn.so.
+ *
+ * The library computes one gated delta-rule linear-attention layer core: the
+ * per-token, per-value-head recurrence on an fp32 state S[dv][dk]
+ *
+ *     S <- exp(g) * S;   p = S k;   d = beta * (v - p);   S <- S + d k^T;   o = (S q) / sqrt(dk)
+ *
+ * (module doc of docs.rs ferrox-core 0.24.0 src/gdn.rs, `delta_step`; CPU reference
+ * `cpu_segment` of docs.rs ferrum-kernels 0.8.0
+ * src/backend/metal/vnext_ops/gated_delta_attention_tests.rs), plus the ops that
+ * surround it in that reference: depthwise causal conv + SiLU with carried raw
+ * inputs, L2 norm of q and k, the softplus/sigmoid gates, the grouped or tiled
+ * k-head map, and the gated RMS norm of the output.
+ *
+ * Conventions shared by every entry point
+ *  - Every array pointer is a DEVICE pointer unless its comment says "host".
+ *    The caller owns all memory; the library allocates nothing and keeps no
+ *    state between calls.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream). Results are visible after the stream is synchronised. Calls are
+ *    reentrant; calls that share output or state buffers must be ordered by the
+ *    caller (same stream or events).
+ *  - All arguments are validated on the host before any HIP call. A call that
+ *    returns an error status has launched nothing and changed no buffer.
+ *    GDN_ERR_LAUNCH is the only status reported after a launch was attempted.
+ *  - Nothing aborts, prints or throws across this interface.
+ *  - dtypes: activations may be f32, f16 or bf16 (gdn_dtype); states, gates given
+ *    as g/beta, decay parameters, dt_bias and norm weights are f32.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a pointer the configuration needs is NULL */
+    GDN_ERR_SHAPE = 2,       /* inconsistent sizes: counts < 0, Hv % Hk != 0, bad cu_seqlens */
+    GDN_ERR_UNSUPPORTED = 3, /* valid but not built: head dims, conv width, dtype, flags */
+    GDN_ERR_OVERFLOW = 4,    /* an element count or offset exceeds what the kernels index */
+    GDN_ERR_ALIGN = 5,       /* a pointer or stride breaks the alignment a kernel needs */
+    GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query returned */
+    GDN_ERR_LAUNCH = 7       /* the HIP runtime reported an error for a launch */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
+
+/* Which k-head v-head h reads (docs.rs ferrox-core src/gdn.rs `HeadMap`;
+ * ferrum-kernels tests page `GatedDeltaValueHeadMapping`):
+ *   GROUPED: h / (Hv / Hk)   (Qwen3-Next order)
+ *   TILED:   h % Hk          (Qwen3.5 order; "interleaved by key head")          */
+typedef enum gdn_head_map { GDN_MAP_GROUPED = 0, GDN_MAP_TILED = 1 } gdn_head_map;
+
+/* How the per-head decay parameter becomes the rate that multiplies softplus
+ * (ferrum-kernels tests page, `cpu_segment` gate section):
+ *   LOG_RATE:      rate = -exp(decay_param[h])   (decay_param is A_log)
+ *   NEGATIVE_RATE: rate = decay_param[h]         (decay_param is -exp(A_log))   */
+typedef enum gdn_decay { GDN_DECAY_LOG_RATE = 0, GDN_DECAY_NEGATIVE_RATE = 1 } gdn_decay;
+
+/* gdn_dims.flags */
+enum {
+    /* q, k rows are normalised in-op: x * (sum x^2 + l2_eps)^(-1/2) per (token,
+     * k-head) (ferrum-kernels tests page, `normalize_rows` and `cpu_segment`). */
+    GDN_L2NORM_QK = 1u,
+    /* gates from raw a, b: g = rate * softplus(a + dt_bias), beta = sigmoid(b)
+     * (softplus with the +-20 cut-overs of that page's `softplus`). Without this
+     * flag the caller passes g and beta directly. */
+    GDN_RAW_GATES = 2u,
+    /* output y = o * (mean_j o_j^2 + norm_eps)^(-1/2) * norm_weight * silu(z)
+     * over the dv values of each (token, v-head) (that page's `cpu_segment`
+     * output section). Without it the output is the core o itself. */
+    GDN_GATED_NORM = 4u
+};
+
+typedef struct gdn_dims {
+    int32_t num_k_heads; /* Hk >= 1 */
+    int32_t num_v_heads; /* Hv >= 1, Hv % Hk == 0 */
+    int32_t head_dim_k;  /* dk */
+    int32_t head_dim_v;  /* dv; built pairs: (dk, dv) in {(32,32), (64,64), (128,128)} */
+    int32_t head_map;    /* gdn_head_map */
+    int32_t decay;       /* gdn_decay, used with GDN_RAW_GATES */
+    uint32_t flags;      /* GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM */
+    float scale;         /* read-out scale; 0 selects 1/sqrt(dk) */
+    float l2_eps;        /* 0 selects 1e-6 */
+    float norm_eps;      /* 0 selects 1e-6 */
+} gdn_dims;
+
+/* Per-token activations. A "token row" r indexes tokens: r = b * T + t for the
+ * decode step (sequence b, token t of T) and the packed token index for the
+ * prefill. Element (row r, head, i) of q is at q[r * q_stride + head * dk + i]
+ * (same for k with k_stride, v with v_stride and dv), so q, k, v may be strided
+ * views into one mixed [tokens][2*Hk*dk + Hv*dv] row. Strides are in elements. */
+typedef struct gdn_inputs {
+    const void *q, *k, *v;
+    int64_t q_stride, k_stride, v_stride;
+    int32_t qkv_dtype;      /* gdn_dtype of q, k, v */
+    /* GDN_RAW_GATES: a, b [tokens][Hv] contiguous in ab_dtype; decay_param and
+     * dt_bias [Hv] f32. */
+    const void *a, *b;
+    int32_t ab_dtype;
+    const float *decay_param, *dt_bias;
+    /* no GDN_RAW_GATES: g (log decay, <= 0 in a real layer) and beta [tokens][Hv] f32 */
+    const float *g, *beta;
+    /* GDN_GATED_NORM: z [tokens][Hv][dv] contiguous in z_dtype; norm_weight [dv] f32 */
+    const void *z;
+    int32_t z_dtype;
+    const float *norm_weight;
+} gdn_inputs;
+
+/* ---------------------------------------------------------------------------
+ * gdn_conv_update -- depthwise causal conv1d + SiLU with carried raw inputs.
+ * (ferrum-kernels tests page, `cpu_segment` conv section; docs.rs libmir-metal
+ * 0.1.0 src/engine/gated_delta_layer/decode/mod.rs, `convolve`.)
+ *
+ * For sequence i with tokens [cu[i], cu[i+1]) and each channel c:
+ *   y[r][c] = silu( sum_{m<K} weight[c][m] * xhat(t + m - (K-1)) ),  t = r - cu[i]
+ * where xhat(j) = x[cu[i] + j][c] for j >= 0 and conv_state[i][c][(K-1) + j]
+ * otherwise; afterwards conv_state[i][c][:] holds the last K-1 entries of
+ * [old state || this call's inputs], oldest first. No bias. A zero-length
+ * sequence leaves its state untouched.
+ *
+ *   channels      C >= 1
+ *   kernel_size   K, 2 <= K <= 8
+ *   num_seqs      N >= 0
+ *   cu_seqlens    device int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = total_tokens;
+ *                 NULL means every sequence has total_tokens / N tokens (N must divide it)
+ *   x             [total_tokens] rows of x_stride elements (>= C), x_dtype
+ *   weight        [C][K] in x_dtype
+ *   conv_state    [N][C][K-1] in x_dtype, updated in place
+ *   y             [total_tokens] rows of y_stride elements (>= C), y_dtype; may not alias x
+ * Errors: NULL, SHAPE (counts, strides), UNSUPPORTED (K, dtype), OVERFLOW.
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_conv_update(int32_t channels, int32_t kernel_size, int32_t num_seqs,
+                           const int32_t *cu_seqlens, int32_t total_tokens, int32_t x_dtype,
+                           const void *x, int64_t x_stride, const void *weight, void *conv_state,
+                           int32_t y_dtype, void *y, int64_t y_stride, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * gdn_decode_step -- the recurrence for `batch` independent sequences of
+ * `tokens_per_seq` tokens each, token order preserved, each sequence's state
+ * read from HBM once and written once per call (ferrox-core src/gdn.rs
+ * `delta_step` for one token; ferrum-kernels tests page `cpu_segment` for the
+ * token loop, the gates and the gated norm).
+ *
+ *   dims            see gdn_dims; flags select L2 norm, raw gates, gated norm
+ *   batch           B >= 0 sequences
+ *   tokens_per_seq  T >= 1; token row of (b, t) is b*T + t
+ *   in              activations; see gdn_inputs
+ *   state           [num_slots][Hv][dv][dk] f32, key index innermost, 16-byte
+ *                   aligned; updated in place
+ *   state_slots     device int32 [B]: slot of sequence b; NULL means slot b.
+ *                   A slot outside [0, num_slots) leaves that sequence's state
+ *                   and output rows untouched.
+ *   num_slots       number of state slots (>= B when state_slots is NULL)
+ *   out_dtype, out  [B*T][Hv][dv]; may not alias any input or the state
+ * Errors: NULL, SHAPE, UNSUPPORTED (dims, dtype), OVERFLOW, ALIGN (state), LAUNCH.
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
+                           const gdn_inputs *in, float *state, const int32_t *state_slots,
+                           int32_t num_slots, int32_t out_dtype, void *out, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * gdn_prefill_workspace_bytes -- device workspace gdn_prefill_chunked needs for
+ * at most num_seqs sequences and total_tokens packed tokens (an upper bound
+ * over every split of total_tokens into num_seqs lengths). Returns 0 when the
+ * arguments are invalid.
+ * ------------------------------------------------------------------------- */
+size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_seqs, int32_t total_tokens);
+
+/* ---------------------------------------------------------------------------
+ * gdn_prefill_chunked -- the same recurrence over packed variable-length
+ * sequences, computed chunk-parallel (64-token chunks that start at each
+ * sequence's first token and never straddle two sequences). The result equals
+ * the token-by-token recurrence up to rounding order (ferrox-core src/gdn.rs
+ * module doc: the chunked form is the same recurrence summed in another order;
+ * ferrum-kernels tests page, `chunked_c64_matches_recurrent_oracle_and_
+ * non_aligned_state_continuity`).
+ *
+ *   num_seqs         N >= 0
+ *   cu_seqlens_host  host int32 [N+1] (validated: cu[0] = 0, non-decreasing,
+ *                    cu[N] = total_tokens)
+ *   cu_seqlens_dev   device int32 [N+1], the same values
+ *   in               activations indexed by packed token row
+ *   state            [N][Hv][dv][dk] f32: initial state in, final state out
+ *   out_dtype, out   [total_tokens][Hv][dv]
+ *   workspace        device, >= gdn_prefill_workspace_bytes(dims, N, total_tokens),
+ *                    256-byte aligned; contents are scratch
+ * Errors: NULL, SHAPE, UNSUPPORTED, OVERFLOW, ALIGN, WORKSPACE, LAUNCH.
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
+                               const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                               int32_t total_tokens, const gdn_inputs *in, float *state,
+                               int32_t out_dtype, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gdn_status_string(gdn_status status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */
