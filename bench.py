@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule step on one MI355X (gfx950).
+
+Default workload (the headline one): batched decode, B=64 independent sequences
+of one token each, Hk=16, Hv=32, dk=dv=128, tiled k-head map, bf16 activations
+drawn N(0,1), fp32 state N(0, 0.02^2), conv width 4 with carried state. One step
+is one pass of the whole decode path: gdn_conv_update (depthwise conv + SiLU,
+state carry) then gdn_decode_step (split, L2 norm of q/k, gates, recurrence,
+gated RMS norm fused). The same inputs are reused every step; the state evolves.
+
+Metric: decode state GB/s = 2 * B * Hv * dv * dk * 4 bytes (the fp32 state read
+and written once) / step time, the definition of the ferrox-core gdn.rs
+throughput probe. Also reported on the same JSON line:
+  * roofline: the decode kernel's algorithmic bytes per launch / its average
+    duration (HIP events around every decode launch in the timed region), against
+    the 8 TB/s HBM peak; traffic from the committed rocprofv3 FETCH/WRITE counter
+    summary when it was taken on the current kernel source, else null;
+  * rotating: the same step cycling through 4 independent state sets (537 MB,
+    larger than the 256 MB Infinity Cache), so the state cannot stay cached;
+  * prefill: chunked prefill tokens/s at B=1, T=4096 (when built);
+  * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "decode state GB/s (% HBM peak); prefill tokens/s at Hv=32,d=128"
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_deltanet_linear_step_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(summary_name, source_hash):
+    """Bytes per dispatch from a committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", summary_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_hash:
+        return None
+    return float(t.group(1))
+
+
+def decode_bench(args, torch, ops, synth):
+    dev = torch.device("cuda:0")
+    B, Hk, Hv, d = 64, 16, 32, 128
+    QK = Hk * d
+    sets = []
+    nsets = 4
+    for i in range(nsets):
+        W = synth.decode_batch(seed=2 + 1000 * i, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d,
+                               head_map=synth.TILED)
+        S = {k: (v.to(dev).contiguous() if hasattr(v, "to") else v) for k, v in W.items()}
+        S["y"] = torch.empty((B, 2 * QK + Hv * d), dtype=torch.float32, device=dev)
+        S["out"] = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
+        S["conv"] = ops.prepare_conv_update(S["x"], S["conv_w"], S["conv_state"], S["y"])
+        y = S["y"]
+        S["dec"] = ops.prepare_decode_step(
+            y[:, :QK], y[:, QK:2 * QK], y[:, 2 * QK:], S["state"], S["out"], Hk=Hk, Hv=Hv,
+            dk=d, dv=d, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
+            decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"])
+        sets.append(S)
+    main = sets[0]
+
+    def step(S, ev=None):
+        S["conv"].launch()
+        if ev is not None:
+            ev[0].record()
+        S["dec"].launch()
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step(main)
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        step(main, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t0.elapsed_time(t1) / K
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+
+    state_bytes = 2 * B * Hv * d * d * 4
+    # decode kernel algorithmic bytes: state r+w, q/k/v read (f32 conv output),
+    # z read (bf16), a/b read (bf16), output write (bf16), per-head params
+    act_bytes = B * (2 * QK + Hv * d) * 4 + B * Hv * d * 2 + 2 * B * Hv * 2 + B * Hv * d * 2 \
+        + Hv * 4 * 2 + d * 4
+    dec_bytes = state_bytes + act_bytes
+    value = state_bytes / (ms_step * 1e-3) / 1e9
+
+    # rotating variant: 4 state sets, > Infinity Cache
+    for _ in range(nsets * 4):
+        for S in sets:
+            step(S)
+    Kr = max(nsets, (K // nsets) * nsets)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record()
+    for i in range(Kr):
+        step(sets[i % nsets])
+    r1.record()
+    torch.cuda.synchronize()
+    ms_rot = r0.elapsed_time(r1) / Kr
+
+    src_hash = kernel_source_hash(["gdn_decode.hip", "gdn_device.h", "gdn_kernels.h"])
+    traffic = read_traffic("decode_b64_bf16_traffic.md", src_hash)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    res = dict(
+        value=value, ms_per_step=ms_step, wall_s=wall,
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic,
+                      kernel="gdn decode_kernel<dk=128,dv=128,waves=8,bf16>", bytes_per_launch=dec_bytes,
+                      avg_launch_us=dec_ms * 1e3, kernel_source_sha256_16=src_hash),
+        rotating=dict(sets=nsets, footprint_mb=nsets * (state_bytes // 2) / 1e6,
+                      ms_per_step=ms_rot,
+                      value=state_bytes / (ms_rot * 1e-3) / 1e9, unit="GB/s"),
+        config=dict(workload="batched decode: B=64 x 1 token, Hk=16, Hv=32, dk=dv=128, tiled map, "
+                             "bf16 N(0,1) activations, fp32 state N(0,0.02^2), conv K=4",
+                    batch=B, tokens_per_seq=1, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map="tiled",
+                    act_dtype="bf16", state_dtype="f32", out_dtype="bf16",
+                    step="gdn_conv_update + gdn_decode_step"),
+    )
+    return res
+
+
+def cpu_baseline(seconds):
+    """The f64 CPU oracle on the decode workload, B=64, for >= `seconds` of work."""
+    import numpy as np
+    import oracle
+    from gated_deltanet_linear_step_amd import synth
+
+    B, Hk, Hv, d = 64, 16, 32, 128
+    W = synth.decode_batch(seed=2, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED)
+    f = lambda t: t.double().numpy()  # noqa: E731
+    threads = max(1, min(16, os.cpu_count() or 1))
+    S, cs = f(W["state"]), f(W["conv_state"])
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        _, cs, S = oracle.batch(B=B, T=1, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=oracle.MAP_TILED,
+                                S0=S, a=f(W["a"]), b=f(W["b"]), decay_param=f(W["A_log"]),
+                                dt_bias=f(W["dt_bias"]), z=f(W["z"]), norm_w=f(W["norm_w"]),
+                                x=f(W["x"]), conv_w=f(W["conv_w"]), conv_state=cs,
+                                nthreads=threads)
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / steps
+    state_bytes = 2 * B * Hv * d * d * 4
+    return dict(value=state_bytes / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                ms_per_step=dt * 1e3,
+                sample=f"{steps} decode steps of the B=64 workload (conv + core, f64 oracle, "
+                       f"{threads} threads over sequences); GB/s counts fp32 state bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_linear_step_amd import ops, synth
+    ops.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    print(f"[bench] decode B=64: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    dec = decode_bench(args, torch, ops, synth)
+    print(f"[bench] decode {dec['value']:.1f} GB/s, {dec['ms_per_step'] * 1e3:.2f} us/step",
+          file=sys.stderr, flush=True)
+    line = dict(metric=METRIC, value=round(dec["value"], 2), unit="GB/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=dec["ms_per_step"],
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                data="synthetic", config=dec["config"],
+                pct_hbm_peak=round(100 * dec["value"] / HBM_PEAK_GBS, 2),
+                roofline=dec["roofline"], rotating=dec["rotating"])
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,19 +17,25 @@ SOURCES = ["gdn_api.cpp", "gdn_conv.hip", "gdn_decode.hip", "gdn_prefill.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-x", "hip"] + srcs + ["-o", LIB + ".tmp"]
+           ] + [f"-D{d}" for d in defines] + ["-x", "hip"] + srcs + ["-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the gfx950 packed-fp32 feature; drop that notice
+    for line in (res.stdout + res.stderr).splitlines():
+        if "packed-fp32-ops" not in line and "unused during compilation" not in line:
+            print(line, file=sys.stderr)
+    if res.returncode != 0:
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

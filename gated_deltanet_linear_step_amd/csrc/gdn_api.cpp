@@ -69,8 +69,12 @@ gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dty
             return GDN_ERR_UNSUPPORTED;
         if (d->decay != GDN_DECAY_LOG_RATE && d->decay != GDN_DECAY_NEGATIVE_RATE)
             return GDN_ERR_SHAPE;
+        if (!aligned(in->a, 4) || !aligned(in->b, 4))
+            return GDN_ERR_ALIGN;  // gates are read as aligned 32-bit words
     } else if (!in->g || !in->beta) {
         return GDN_ERR_NULL;
+    } else if (!aligned(in->g, 4) || !aligned(in->beta, 4)) {
+        return GDN_ERR_ALIGN;
     }
     if (d->flags & GDN_GATED_NORM) {
         if (!in->z || !in->norm_weight)

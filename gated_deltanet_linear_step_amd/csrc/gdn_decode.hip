@@ -20,18 +20,76 @@
 //        p_j = a (S_j.k),  o_j = scale (a (S_j.q) + d_j (k.q)),
 //    which is S_new.q expanded -- the same value in another rounding order (the
 //    ferrox-core page notes this expansion next to its throughput probe).
-//  * v for the token is staged in LDS; outputs are gathered in LDS and the gated
-//    RMS norm runs over them after the token group.
+//  * a token's activations are loaded before anything that waits on them; v
+//    arrives one element per lane and is spread to the rows by shuffles. The
+//    outputs are gathered in LDS and the gated RMS norm runs over them after
+//    each group of tokens.
 
 #include "gdn_device.h"
 #include "gdn_kernels.h"
+
+#ifndef GDN_DECODE_NW
+#define GDN_DECODE_NW 8  // waves per workgroup for the 128 x 128 state
+#endif
+#ifndef GDN_NT_LOAD
+#define GDN_NT_LOAD 0  // 1: non-temporal state loads
+#endif
+#ifndef GDN_NT_STORE
+#define GDN_NT_STORE 0  // 1: non-temporal state stores
+#endif
 
 namespace gdn {
 namespace {
 
 constexpr int kTokGroup = 8;  // tokens whose outputs are buffered in LDS at once
 
-template <int DK, int DV, int NW>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_state4(const float *p)
+{
+#if GDN_NT_LOAD
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+#else
+    f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#endif
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_state4(float *p, float4 s)
+{
+    f32x4 v = {s.x, s.y, s.z, s.w};
+#if GDN_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+#else
+    *reinterpret_cast<f32x4 *>(p) = v;
+#endif
+}
+
+// Activations of one token for one wave, as raw bits: the k and q pieces, the
+// two gate words (raw a/b or given g/beta) and one v element per lane. Loading
+// and converting are separate so the state loads can be issued in between.
+template <int QT>
+struct TokenRaw {
+    Raw4<QT> k, q;
+    uint32_t ga, gb, v;
+};
+
+template <int DK, int DV, int QT>
+__device__ __forceinline__ void load_token(TokenRaw<QT> &t, const DecodeParams &p, int64_t r,
+                                           int h, int kh, int col, int vrow)
+{
+    const ActInputs &in = p.in;
+    const int Hv = p.hc.Hv;
+    t.k = load_raw4<QT>(in.k, r * in.k_stride + (int64_t)kh * DK + col);
+    t.q = load_raw4<QT>(in.q, r * in.q_stride + (int64_t)kh * DK + col);
+    const bool raw = p.hc.flags & F_RAW_GATES;
+    const int gdt = raw ? in.ab_dt : DT_F32;
+    t.ga = load_word_nb(raw ? in.a : (const void *)in.g, r * Hv + h, gdt);
+    t.gb = load_word_nb(raw ? in.b : (const void *)in.beta, r * Hv + h, gdt);
+    t.v = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DV + vrow);
+}
+
+template <int DK, int DV, int NW, int QT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
 {
     constexpr int LPR = DK / 4;       // lanes holding one row
@@ -39,12 +97,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     constexpr int RPW = DV / NW;      // rows per wave
     constexpr int NI = RPW / RPI;     // float4 row pieces per lane
     static_assert(DK % 4 == 0 && 64 % LPR == 0 && RPW % RPI == 0 && NI >= 1, "shape");
+    static_assert(RPW <= 64, "one v value per lane covers the wave's rows");
 
-    __shared__ float v_s[kTokGroup][DV];
     __shared__ float o_s[kTokGroup][DV];
 
     const HeadCfg &hc = p.hc;
-    const ActInputs &in = p.in;
     const int Hv = hc.Hv;
     const int h = blockIdx.x % Hv;
     const int b = blockIdx.x / Hv;
@@ -57,82 +114,75 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     const int sub = lane / LPR;
     const int col = (lane % LPR) * 4;
     const uint32_t flags = hc.flags;
-
-    float *Sg = p.state + ((int64_t)slot * Hv + h) * (int64_t)(DV * DK);
     const int row0 = wave * RPW + sub;
-
-    float4 S[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-        S[i] = *reinterpret_cast<const float4 *>(Sg + (row0 + i * RPI) * DK + col);
+    const int vrow = wave * RPW + (lane % RPW);  // the v element this lane fetches
 
     float dec_rate = 0.f, dtb = 0.f;
     if (flags & F_RAW_GATES) {
-        float dp = in.decay_param[h];
+        const float dp = p.in.decay_param[h];
         dec_rate = hc.decay_kind == 0 ? -expf(dp) : dp;
-        dtb = in.dt_bias[h];
+        dtb = p.in.dt_bias[h];
     }
 
-    for (int t0 = 0; t0 < p.T; t0 += kTokGroup) {
-        const int tn = min(kTokGroup, p.T - t0);
-        for (int idx = threadIdx.x; idx < tn * DV; idx += NW * 64) {
-            const int tt = idx / DV, j = idx % DV;
-            const int64_t r = (int64_t)b * p.T + t0 + tt;
-            v_s[tt][j] = load_act(in.v, r * in.v_stride + (int64_t)h * DV + j, in.qkv_dt);
+    // Token 0's activations are issued before the state: vector-memory returns
+    // are counted in order, so the prologue math can run while the state is in
+    // flight, and each row piece is processed as soon as it lands.
+    TokenRaw<QT> tr;
+    load_token<DK, DV, QT>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
+    __builtin_amdgcn_sched_barrier(0);  // keep the token loads ahead of the state loads
+
+    float *Sg = p.state + ((int64_t)slot * Hv + h) * (int64_t)(DV * DK);
+    float4 S[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        S[i] = load_state4(Sg + (row0 + i * RPI) * DK + col);
+    __builtin_amdgcn_sched_barrier(0);  // ... and their use behind the state loads
+    const bool raw_gates = flags & F_RAW_GATES;
+    const int gdt = raw_gates ? p.in.ab_dt : DT_F32;
+
+    // One token through this wave's rows: prologue (norms, gates), then the two
+    // reductions, the update and the read-out per row piece; outputs go to
+    // o_s[tt] for the group epilogue.
+    auto process_token = [&](int tt, int64_t r) {
+        float4 kk = raw4_to_f32<QT>(tr.k), qq = raw4_to_f32<QT>(tr.q);
+        if (flags & F_L2NORM) {
+            const float sk = group_sum<LPR>(dot4(kk, kk));
+            const float sq = group_sum<LPR>(dot4(qq, qq));
+            const float ik = rsqrtf(sk + hc.l2_eps), iq = rsqrtf(sq + hc.l2_eps);
+            kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
+            qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
         }
-        __syncthreads();
-
-        for (int tt = 0; tt < tn; ++tt) {
-            const int64_t r = (int64_t)b * p.T + t0 + tt;
-            float4 kk = load_act4(in.k, r * in.k_stride + (int64_t)kh * DK + col, in.qkv_dt);
-            float4 qq = load_act4(in.q, r * in.q_stride + (int64_t)kh * DK + col, in.qkv_dt);
-            if (flags & F_L2NORM) {
-                const float sk = group_sum<LPR>(dot4(kk, kk));
-                const float sq = group_sum<LPR>(dot4(qq, qq));
-                const float ik = rsqrtf(sk + hc.l2_eps), iq = rsqrtf(sq + hc.l2_eps);
-                kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
-                qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
-            }
-            float g, beta;
-            if (flags & F_RAW_GATES) {
-                const float av = load_act(in.a, r * Hv + h, in.ab_dt);
-                const float bv = load_act(in.b, r * Hv + h, in.ab_dt);
-                g = dec_rate * softplus_f(av + dtb);
-                beta = sigmoid_f(bv);
-            } else {
-                g = in.g[r * Hv + h];
-                beta = in.beta[r * Hv + h];
-            }
-            const float alpha = expf(g);
-            const float kq = group_sum<LPR>(dot4(kk, qq));
-
-            float pk[NI], pq[NI];
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                pk[i] = dot4(S[i], kk);
-                pq[i] = dot4(S[i], qq);
-            }
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                pk[i] = group_sum<LPR>(pk[i]);
-                pq[i] = group_sum<LPR>(pq[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int row = row0 + i * RPI;
-                const float d = beta * (v_s[tt][row] - alpha * pk[i]);
-                const float o = hc.scale * (alpha * pq[i] + d * kq);
-                S[i].x = fmaf(alpha, S[i].x, d * kk.x);
-                S[i].y = fmaf(alpha, S[i].y, d * kk.y);
-                S[i].z = fmaf(alpha, S[i].z, d * kk.z);
-                S[i].w = fmaf(alpha, S[i].w, d * kk.w);
-                if (col == 0)
-                    o_s[tt][row] = o;
-            }
+        const float ga = word_to_f32(tr.ga, r * Hv + h, gdt);
+        const float gb = word_to_f32(tr.gb, r * Hv + h, gdt);
+        float g, beta;
+        if (raw_gates) {
+            g = dec_rate * softplus_f(ga + dtb);
+            beta = sigmoid_f(gb);
+        } else {
+            g = ga;
+            beta = gb;
         }
-        __syncthreads();
+        const float alpha = expf(g);
+        const float kq = group_sum<LPR>(dot4(kk, qq));
+        const float vv = raw1_to_f32<QT>(tr.v);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float pk = group_sum<LPR>(dot4(S[i], kk));
+            const float pq = group_sum<LPR>(dot4(S[i], qq));
+            const float vj = __shfl(vv, sub + i * RPI, 64);
+            const float d = beta * (vj - alpha * pk);
+            const float o = hc.scale * (alpha * pq + d * kq);
+            S[i].x = fmaf(alpha, S[i].x, d * kk.x);
+            S[i].y = fmaf(alpha, S[i].y, d * kk.y);
+            S[i].z = fmaf(alpha, S[i].z, d * kk.z);
+            S[i].w = fmaf(alpha, S[i].w, d * kk.w);
+            if (col == 0)
+                o_s[tt][row0 + i * RPI] = o;
+        }
+    };
 
-        // epilogue: one wave per token of the group
+    // Gated RMS norm (or plain copy) of the tokens [t0, t0 + tn): one wave per token.
+    auto epilogue = [&](int t0, int tn) {
         for (int tt = wave; tt < tn; tt += NW) {
             const int64_t r = (int64_t)b * p.T + t0 + tt;
             const int64_t obase = (r * Hv + h) * DV;
@@ -143,27 +193,47 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
                 ss = group_sum<64>(ss);
                 const float inv = rsqrtf(ss / (float)DV + hc.norm_eps);
                 for (int j = lane; j < DV; j += 64) {
-                    const float zv = load_act(in.z, obase + j, in.z_dt);
-                    store_act(p.out, obase + j, p.out_dt, o_s[tt][j] * inv * in.norm_w[j] * silu_f(zv));
+                    const float zv = load_act(p.in.z, obase + j, p.in.z_dt);
+                    store_act(p.out, obase + j, p.out_dt,
+                              o_s[tt][j] * inv * p.in.norm_w[j] * silu_f(zv));
                 }
             } else {
                 for (int j = lane; j < DV; j += 64)
                     store_act(p.out, obase + j, p.out_dt, o_s[tt][j]);
             }
         }
-        __syncthreads();
-    }
+    };
 
+    // token 0 in straight-line code, so each row piece is used as soon as it lands
+    process_token(0, (int64_t)b * p.T);
+    for (int t = 1; t < p.T; ++t) {
+        const int tt = t % kTokGroup;
+        if (tt == 0) {  // o_s holds a full group: drain it
+            __syncthreads();
+            epilogue(t - kTokGroup, kTokGroup);
+            __syncthreads();
+        }
+        const int64_t r = (int64_t)b * p.T + t;
+        load_token<DK, DV, QT>(tr, p, r, h, kh, col, vrow);
+        process_token(tt, r);
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-        *reinterpret_cast<float4 *>(Sg + (row0 + i * RPI) * DK + col) = S[i];
+        store_state4(Sg + (row0 + i * RPI) * DK + col, S[i]);
+    __syncthreads();
+    const int tlast0 = ((p.T - 1) / kTokGroup) * kTokGroup;
+    epilogue(tlast0, p.T - tlast0);
 }
 
 template <int DK, int DV, int NW>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)p.B * p.hc.Hv;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, p);
+    const dim3 grid((unsigned)((int64_t)p.B * p.hc.Hv)), block(NW * 64);
+    switch (p.in.qkv_dt) {
+    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32>), grid, block, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16>), grid, block, 0, s, p); break;
+    }
     return hipGetLastError();
 }
 
@@ -179,7 +249,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
     if (p.B == 0)
         return hipSuccess;
     if (p.hc.dk == 128 && p.hc.dv == 128)
-        return launch_decode_t<128, 128, 4>(p, s);
+        return launch_decode_t<128, 128, GDN_DECODE_NW>(p, s);
     if (p.hc.dk == 64 && p.hc.dv == 64)
         return launch_decode_t<64, 64, 4>(p, s);
     if (p.hc.dk == 32 && p.hc.dv == 32)

@@ -61,6 +61,104 @@ __device__ __forceinline__ float4 load_act4(const void *p, int64_t idx, int dt)
                        f16_bits_to_f32(w.y & 0xffffu), f16_bits_to_f32(w.y >> 16));
 }
 
+// Compile-time-dtype loads for the hot paths: no branch sits between a load
+// and the next one, so independent loads stay in flight together.
+template <int DT>
+__device__ __forceinline__ float load_act_t(const void *p, int64_t idx)
+{
+    if constexpr (DT == DT_F32)
+        return static_cast<const float *>(p)[idx];
+    const uint32_t h = static_cast<const uint16_t *>(p)[idx];
+    if constexpr (DT == DT_BF16)
+        return bf16_bits_to_f32(h);
+    return f16_bits_to_f32(h);
+}
+
+template <int DT>
+__device__ __forceinline__ float4 load_act4_t(const void *p, int64_t idx)
+{
+    if constexpr (DT == DT_F32)
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + idx);
+    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + idx);
+    if constexpr (DT == DT_BF16)
+        return make_float4(bf16_bits_to_f32(w.x & 0xffffu), bf16_bits_to_f32(w.x >> 16),
+                           bf16_bits_to_f32(w.y & 0xffffu), bf16_bits_to_f32(w.y >> 16));
+    return make_float4(f16_bits_to_f32(w.x & 0xffffu), f16_bits_to_f32(w.x >> 16),
+                       f16_bits_to_f32(w.y & 0xffffu), f16_bits_to_f32(w.y >> 16));
+}
+
+// One element of runtime dtype `dt`, read without a branch: the 32-bit word
+// holding it is loaded (the base pointer is 4-byte aligned -- the host checks),
+// then the conversion is selected. Split into the load and the conversion so a
+// caller can issue other loads in between.
+__device__ __forceinline__ uint32_t load_word_nb(const void *p, int64_t idx, int dt)
+{
+    const int64_t byte = dt == DT_F32 ? idx * 4 : idx * 2;
+    return *reinterpret_cast<const uint32_t *>(static_cast<const char *>(p) + (byte & ~(int64_t)3));
+}
+
+__device__ __forceinline__ float word_to_f32(uint32_t w, int64_t idx, int dt)
+{
+    const uint32_t h = (idx & 1) ? (w >> 16) : (w & 0xffffu);
+    const float vf16 = f16_bits_to_f32(h), vbf16 = bf16_bits_to_f32(h);
+    return dt == DT_F32 ? __uint_as_float(w) : (dt == DT_BF16 ? vbf16 : vf16);
+}
+
+// Raw bits of four consecutive activations of compile-time dtype DT (8 bytes for
+// 16-bit types, 16 for f32) and their conversion.
+template <int DT>
+struct Raw4 {
+    uint32_t w[DT == DT_F32 ? 4 : 2];
+};
+
+template <int DT>
+__device__ __forceinline__ Raw4<DT> load_raw4(const void *p, int64_t idx)
+{
+    Raw4<DT> r;
+    if constexpr (DT == DT_F32) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p) + idx);
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + idx);
+        r.w[0] = v.x; r.w[1] = v.y;
+    }
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ float4 raw4_to_f32(const Raw4<DT> &r)
+{
+    if constexpr (DT == DT_F32)
+        return make_float4(__uint_as_float(r.w[0]), __uint_as_float(r.w[1]),
+                           __uint_as_float(r.w[2]), __uint_as_float(r.w[3]));
+    else if constexpr (DT == DT_BF16)
+        return make_float4(bf16_bits_to_f32(r.w[0] & 0xffffu), bf16_bits_to_f32(r.w[0] >> 16),
+                           bf16_bits_to_f32(r.w[1] & 0xffffu), bf16_bits_to_f32(r.w[1] >> 16));
+    else
+        return make_float4(f16_bits_to_f32(r.w[0] & 0xffffu), f16_bits_to_f32(r.w[0] >> 16),
+                           f16_bits_to_f32(r.w[1] & 0xffffu), f16_bits_to_f32(r.w[1] >> 16));
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw1(const void *p, int64_t idx)
+{
+    if constexpr (DT == DT_F32)
+        return static_cast<const uint32_t *>(p)[idx];
+    else
+        return static_cast<const uint16_t *>(p)[idx];
+}
+
+template <int DT>
+__device__ __forceinline__ float raw1_to_f32(uint32_t w)
+{
+    if constexpr (DT == DT_F32)
+        return __uint_as_float(w);
+    else if constexpr (DT == DT_BF16)
+        return bf16_bits_to_f32(w);
+    else
+        return f16_bits_to_f32(w);
+}
+
 __device__ __forceinline__ void store_act(void *p, int64_t idx, int dt, float v)
 {
     if (dt == DT_F32)

@@ -13,7 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgdn.so")
+# GDN_LIB_PATH selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("GDN_LIB_PATH") or os.path.join(HERE, "libgdn.so")
 
 GDN_OK = 0
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
@@ -260,3 +261,44 @@ def prefill_chunked(q, k, v, state, cu_seqlens, *, Hk, Hv, dk, dv, head_map, a=N
     _check(st, "gdn_prefill_chunked")
     del keep
     return out
+
+
+class PreparedCall:
+    """A library call with its ctypes arguments built once; ``launch()`` re-issues
+    it on the stream captured at preparation time (for tight timing loops and
+    graph capture, where per-call Python marshalling would dominate)."""
+
+    def __init__(self, fn, args, what, keep):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def launch(self):
+        st = self._fn(*self._args)
+        if st != GDN_OK:
+            raise GdnError(st, self._what)
+
+
+def prepare_conv_update(x, weight, conv_state, y, *, cu_seqlens=None, num_seqs=None,
+                        stream=None) -> PreparedCall:
+    total, C = x.shape
+    N = conv_state.shape[0] if num_seqs is None else num_seqs
+    args = (C, weight.shape[1], N, _ptr(cu_seqlens), total, _dt(x), _ptr(x), x.stride(0),
+            _ptr(weight), _ptr(conv_state), _dt(y), _ptr(y), y.stride(0), _stream(stream))
+    return PreparedCall(load().gdn_conv_update, args, "gdn_conv_update",
+                        [x, weight, conv_state, y, cu_seqlens])
+
+
+def prepare_decode_step(q, k, v, state, out, *, Hk, Hv, dk, dv, head_map, batch,
+                        tokens_per_seq=1, a=None, b=None, decay_param=None, dt_bias=None,
+                        g=None, beta=None, z=None, norm_weight=None, l2norm_qk=True,
+                        decay=DECAY_LOG_RATE, scale=0.0, state_slots=None,
+                        stream=None) -> PreparedCall:
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    args = (ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(inp), _ptr(state),
+            _ptr(state_slots), state.shape[0], _dt(out), _ptr(out), _stream(stream))
+    return PreparedCall(load().gdn_decode_step, args, "gdn_decode_step",
+                        keep + [dims, inp, state, out, state_slots])

@@ -166,8 +166,9 @@ def test_core_given_gates_shapes(d, head_map, T):
 
 @pytest.mark.parametrize("act", [torch.float32, torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_activation_and_output_dtypes(act, out_dtype):
-    B, T = 4, 2
+@pytest.mark.parametrize("T", [1, 2])
+def test_activation_and_output_dtypes(act, out_dtype, T):
+    B = 4
     W = to_dev(synth.decode_batch(seed=7, B=B, T=T, Hk=2, Hv=4, head_map=synth.GROUPED,
                                   dtype=act))
     out = run_layer(W, T=T, B=B, out_dtype=out_dtype)
@@ -247,10 +248,12 @@ def test_error_leaves_buffers_untouched():
     assert torch.equal(st, before) and torch.all(out == 3.0)
 
 
-def test_conv_update_varlen_matches_oracle():
-    rng = np.random.default_rng(22)
-    lengths = [5, 0, 1, 2, 9]
-    C, K = 300, 4
+@pytest.mark.parametrize("K", [2, 4, 6])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.float16])
+def test_conv_update_varlen_matches_oracle(K, y_dtype):
+    rng = np.random.default_rng(22 + K)
+    lengths = [5, 0, 1, 2, 9, 3]
+    C = 300
     total = sum(lengths)
     x = torch.from_numpy(rng.normal(size=(total, C)).astype(np.float32)).to(torch.bfloat16)
     w = torch.from_numpy(rng.normal(0, 0.5, size=(C, K)).astype(np.float32)).to(torch.bfloat16)
@@ -258,11 +261,34 @@ def test_conv_update_varlen_matches_oracle():
         torch.bfloat16)
     cu = synth.cu_seqlens(lengths)
     cs_d = cs.to(DEV)
-    y = ops.conv_update(x.to(DEV), w.to(DEV), cs_d, cu_seqlens=cu.to(DEV))
+    y = ops.conv_update(x.to(DEV), w.to(DEV), cs_d, cu_seqlens=cu.to(DEV), y_dtype=y_dtype)
     torch.cuda.synchronize()
     for i, n in enumerate(lengths):
         lo = int(cu[i])
         yo, so = oracle.conv(f64(x[lo:lo + n]).reshape(n, C), f64(w), f64(cs[i]))
         if n:
-            assert maxabs(f64(y[lo:lo + n]), yo) <= 1e-5
+            err = np.abs(f64(y[lo:lo + n]) - yo)
+            bound = 1e-5 if y_dtype == torch.float32 else ulp16(yo, y_dtype) + 1e-5
+            assert np.all(err <= bound)
+        assert maxabs(f64(cs_d[i]), so) == 0.0
+
+
+@pytest.mark.parametrize("act", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("C", [8192, 300, 302])
+def test_conv_update_one_token_per_sequence(act, y_dtype, C):
+    # the decode shape (vectorised when C % 4 == 0, the generic kernel otherwise)
+    rng = np.random.default_rng(23)
+    N, K = 5, 4
+    x = torch.from_numpy(rng.normal(size=(N, C)).astype(np.float32)).to(act)
+    w = torch.from_numpy(rng.normal(0, 0.5, size=(C, K)).astype(np.float32)).to(act)
+    cs = torch.from_numpy(rng.normal(size=(N, C, K - 1)).astype(np.float32)).to(act)
+    cs_d = cs.to(DEV)
+    y = ops.conv_update(x.to(DEV), w.to(DEV), cs_d, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    for i in range(N):
+        yo, so = oracle.conv(f64(x[i:i + 1]), f64(w), f64(cs[i]))
+        err = np.abs(f64(y[i:i + 1]) - yo)
+        bound = 1e-5 if y_dtype == torch.float32 else ulp16(yo, y_dtype) + 1e-5
+        assert np.all(err <= bound)
         assert maxabs(f64(cs_d[i]), so) == 0.0
