@@ -233,7 +233,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims *d, int32_t num_seqs, int32_t 
         return 0;
     const int64_t max_chunks = (int64_t)total_tokens / gdn::kChunk + num_seqs;
     return gdn::prefill_workspace_bytes(d->num_k_heads, d->num_v_heads, d->head_dim_k,
-                                        d->head_dim_v, max_chunks, num_seqs);
+                                        d->head_dim_v, max_chunks, num_seqs, total_tokens,
+                                        (d->flags & GDN_GATED_NORM) != 0);
 }
 
 gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,

@@ -74,14 +74,16 @@ struct PrefillParams {
     uint16_t *wmat;        // [num_chunks][Hv][64][dk]   f16, W = T diag(beta*gamma) K
     float *umat;           // [num_chunks][Hv][64][dv]   f32, U = T diag(beta) V
     uint16_t *aqk;         // [num_chunks][Hv][64][64]   f16, masked decayed Q K^T
-    float *gam;            // [num_chunks][Hv][64]       f32, gamma_t = exp(G_t)
+    float *gcum;           // [num_chunks][Hv][64]       f32, in-chunk prefix sums G_t of g
+    float *onorm;          // [total][Hv][dv]            f32 core output (gated norm only)
 };
 
 bool decode_supported(int dk, int dv);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
 bool prefill_supported(int dk, int dv);
-size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N);
+size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
+                               int64_t total_tokens, bool norm);
 void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks);
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
 

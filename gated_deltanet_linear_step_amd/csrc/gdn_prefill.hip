@@ -1,12 +1,624 @@
-// gdn_prefill.hip -- chunked prefill (placeholder until the chunk kernels land).
+// gdn_prefill.hip -- chunked prefill of the gated delta rule on gfx950 (MFMA).
+//
+// The recurrence of the decode step, summed chunk by chunk: the ferrox-core
+// 0.24.0 gdn.rs page states that the chunked prefill is the same recurrence in
+// another summation order, and the ferrum-kernels 0.8.0 tests page checks a
+// 64-token chunked core against the token-by-token reference
+// (`chunked_c64_matches_recurrent_oracle_and_non_aligned_state_continuity`).
+// The chunk algebra below is derived from the recurrence itself.
+//
+// Within one chunk of n <= 64 tokens of one v-head, with entering state S0
+// (dv x dk), G_t = g_0 + ... + g_t, gamma_t = exp(G_t):
+//     S_t = gamma_t S0 + sum_{s<=t} exp(G_t - G_s) d_s k_s^T             (unrolled rule)
+//     d_t + sum_{s<t} A_ts d_s = beta_t v_t - beta_t gamma_t S0 k_t,
+//         A_ts = beta_t exp(G_t - G_s) (k_t . k_s)   for s < t
+// so with T = (I + A)^-1, U = T diag(beta) V, W = T diag(beta gamma) K:
+//     D   = U - W S0^T                                (rows d_t)
+//     O   = scale (diag(gamma) Q S0^T + Aqk D),  Aqk_ts = exp(G_t - G_s)(q_t . k_s), s <= t
+//     S_n = gamma_{n-1} S0 + D^T diag(exp(G_{n-1} - G_t)) K
+//
+// Kernels:
+//  1. plan_kernel   -- chunk table: 64-token chunks from each sequence's first
+//                      token (the last may be short; none straddles sequences).
+//  2. prep_kernel   -- per (chunk, v-head), all chunks in parallel: q/k L2 norm,
+//                      gates and their in-chunk prefix sums, the gram K K^T and
+//                      Q K^T (f16 MFMA), T = (I + A)^-1 in f32 (16x16 diagonal
+//                      blocks by substitution, off-diagonal blocks by f32 MFMA
+//                      block products), then U and W (f16 MFMA). Writes U (f32),
+//                      W, Aqk, the normalised Q and K^T (f16) and G to the workspace.
+//  3. carry_kernel  -- per (sequence, v-head, 16-row slice of dv), sequential
+//                      over the sequence's chunks: the state slice stays in MFMA
+//                      accumulators (f32) with an f16 copy in LDS as an operand;
+//                      D, O and the next state per chunk on f16 MFMA with f32
+//                      accumulation. D enters the state update as an f16 hi+lo
+//                      pair. The next chunk's operands are prefetched into VGPRs
+//                      while the current chunk is computed.
+//  4. norm_kernel   -- gated RMS norm of the f32 core output (optional).
+
 #include "gdn_device.h"
 #include "gdn_kernels.h"
 
 namespace gdn {
+namespace {
 
-bool prefill_supported(int, int) { return false; }
-size_t prefill_workspace_bytes(int, int, int, int, int64_t, int) { return 0; }
-void prefill_carve(PrefillParams &, void *, int64_t) {}
-hipError_t launch_prefill(const PrefillParams &, hipStream_t) { return hipErrorNotSupported; }
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = kChunk;     // 64 tokens per chunk
+constexpr int DH = 128;       // head dim (dk = dv) of the built prefill
+constexpr int KP = DH + 8;    // padded f16 row (272 B): conflict-free 16-B MFMA operand reads
+constexpr int TP = C + 8;     // padded f16 row of a transposed [dim][token] tile (144 B)
+constexpr int AP = C + 4;     // padded f32 row of the 64x64 A / T matrix
+constexpr int DT = 16;        // dv rows per carry workgroup
+
+__device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 lds_half8(const _Float16 *p)
+{
+    return *reinterpret_cast<const half8 *>(p);
+}
+
+__device__ __forceinline__ half8 glb_half8(const uint16_t *p)
+{
+    return *reinterpret_cast<const half8 *>(p);
+}
+
+// ---------------------------------------------------------------- workspace
+
+struct WsLayout {
+    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, qn, knT, wmat, umat, aqk, gcum, onorm, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int Hk, int Hv, int64_t MC, int N, int64_t total_tokens, bool norm)
+{
+    WsLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    L.chunk_seq = take(sizeof(int32_t) * MC);
+    L.chunk_start = take(sizeof(int32_t) * MC);
+    L.chunk_len = take(sizeof(int32_t) * MC);
+    L.seq_chunk0 = take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    L.qn = take(sizeof(uint16_t) * MC * Hk * C * DH);
+    L.knT = take(sizeof(uint16_t) * MC * Hk * DH * C);
+    L.wmat = take(sizeof(uint16_t) * MC * Hv * C * DH);
+    L.umat = take(sizeof(float) * MC * Hv * C * DH);
+    L.aqk = take(sizeof(uint16_t) * MC * Hv * C * C);
+    L.gcum = take(sizeof(float) * MC * Hv * C);
+    L.onorm = norm ? take(sizeof(float) * (size_t)total_tokens * Hv * DH) : off;
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------- 1. plan
+
+__global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
+{
+    __shared__ int scan[256];
+    __shared__ int base_s;
+    if (threadIdx.x == 0)
+        base_s = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < p.N; i0 += 256) {
+        const int i = i0 + threadIdx.x;
+        int start = 0, len = 0;
+        if (i < p.N) {
+            start = p.cu[i];
+            len = p.cu[i + 1] - start;
+        }
+        const int nc = (len + C - 1) / C;
+        scan[threadIdx.x] = nc;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
+            const int v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            scan[threadIdx.x] += v;
+            __syncthreads();
+        }
+        const int first = base_s + scan[threadIdx.x] - nc;
+        if (i < p.N) {
+            p.seq_chunk0[i] = first;
+            for (int c = 0; c < nc; ++c) {
+                p.chunk_seq[first + c] = i;
+                p.chunk_start[first + c] = start + c * C;
+                p.chunk_len[first + c] = min(C, len - c * C);
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 255)
+            base_s += scan[255];
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- 2. prep
+
+template <int QT>
+__global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
+{
+    // LDS: X1 = normalised K rows (f16) then A / T (f32, in place);
+    //      X2 = normalised Q rows (f16) then the block-product scratch (f32).
+    __shared__ __attribute__((aligned(16))) unsigned char X1[C * AP * 4];
+    __shared__ __attribute__((aligned(16))) unsigned char X2[C * KP * 2];
+    __shared__ __attribute__((aligned(16))) _Float16 VbT[DH][TP];  // beta_t v_t, transposed
+    __shared__ __attribute__((aligned(16))) _Float16 KbT[DH][TP];  // beta_t gamma_t k_t, transposed
+    __shared__ float G_s[C], beta_s[C];
+    static_assert(C * AP * 4 >= C * KP * 2, "X1 holds both the K rows and A / T");
+    static_assert(C * KP * 2 >= 32 * 36 * 4, "X2 holds the Q rows and the 32x32 scratch");
+
+    _Float16(*Kh)[KP] = reinterpret_cast<_Float16(*)[KP]>(X1);
+    _Float16(*Qh)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);
+    float(*Am)[AP] = reinterpret_cast<float(*)[AP]>(X1);
+    float(*Pm)[36] = reinterpret_cast<float(*)[36]>(X2);
+
+    const HeadCfg &hc = p.hc;
+    const ActInputs &in = p.in;
+    const int Hv = hc.Hv, Hk = hc.Hk;
+    const int chunk = blockIdx.x / Hv;
+    const int h = blockIdx.x % Hv;
+    const int kh = k_head_of(hc.head_map, h, Hk, Hv);
+    const int tok0 = p.chunk_start[chunk];
+    const int n = p.chunk_len[chunk];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t flags = hc.flags;
+    // one of the v-heads reading kh writes the normalised Q and K^T for the carry
+    const bool qk_writer = hc.head_map == 0 ? (h % (Hv / Hk) == 0) : (h < Hk);
+
+    // -- gates and their prefix sums (wave 0, lane = token)
+    if (wave == 0) {
+        float g = 0.f, beta = 0.f;
+        if (lane < n) {
+            const int64_t gi = (int64_t)(tok0 + lane) * Hv + h;
+            if (flags & F_RAW_GATES) {
+                const float dp = in.decay_param[h];
+                const float rate = hc.decay_kind == 0 ? -expf(dp) : dp;
+                g = rate * softplus_f(load_act(in.a, gi, in.ab_dt) + in.dt_bias[h]);
+                beta = sigmoid_f(load_act(in.b, gi, in.ab_dt));
+            } else {
+                g = in.g[gi];
+                beta = in.beta[gi];
+            }
+        }
+        float G = g;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(G, off, 64);
+            if (lane >= off)
+                G += o;
+        }
+        G_s[lane] = G;  // tokens >= n carry G_{n-1} (their g is 0)
+        beta_s[lane] = beta;
+    }
+    __syncthreads();
+
+    // -- rows of k, q, v: wave w loads tokens 16w .. 16w+15, 32 lanes per row
+    {
+        const int sub = lane >> 5, c4 = (lane & 31) * 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = wave * 16 + 2 * i + sub;
+            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), qq = kk, vv = kk;
+            if (t < n) {
+                const int64_t r = tok0 + t;
+                kk = load_act4_t<QT>(in.k, r * in.k_stride + (int64_t)kh * DH + c4);
+                qq = load_act4_t<QT>(in.q, r * in.q_stride + (int64_t)kh * DH + c4);
+                vv.x = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4);
+                vv.y = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4 + 1);
+                vv.z = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4 + 2);
+                vv.w = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4 + 3);
+            }
+            if (flags & F_L2NORM) {
+                const float ik = rsqrtf(group_sum<32>(dot4(kk, kk)) + hc.l2_eps);
+                const float iq = rsqrtf(group_sum<32>(dot4(qq, qq)) + hc.l2_eps);
+                kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
+                qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
+            }
+            Kh[t][c4] = (_Float16)kk.x; Kh[t][c4 + 1] = (_Float16)kk.y;
+            Kh[t][c4 + 2] = (_Float16)kk.z; Kh[t][c4 + 3] = (_Float16)kk.w;
+            Qh[t][c4] = (_Float16)qq.x; Qh[t][c4 + 1] = (_Float16)qq.y;
+            Qh[t][c4 + 2] = (_Float16)qq.z; Qh[t][c4 + 3] = (_Float16)qq.w;
+            const float bt = beta_s[t];
+            const float bg = bt * expf(G_s[t]);
+            VbT[c4][t] = (_Float16)(bt * vv.x); VbT[c4 + 1][t] = (_Float16)(bt * vv.y);
+            VbT[c4 + 2][t] = (_Float16)(bt * vv.z); VbT[c4 + 3][t] = (_Float16)(bt * vv.w);
+            // the f16-rounded normalised k, scaled: the same K the carry multiplies
+            KbT[c4][t] = (_Float16)(bg * (float)(_Float16)kk.x);
+            KbT[c4 + 1][t] = (_Float16)(bg * (float)(_Float16)kk.y);
+            KbT[c4 + 2][t] = (_Float16)(bg * (float)(_Float16)kk.z);
+            KbT[c4 + 3][t] = (_Float16)(bg * (float)(_Float16)kk.w);
+        }
+    }
+    __syncthreads();
+
+    // -- K K^T and Q K^T on the lower block triangle: wave w owns token rows 16w..
+    const int li = lane & 15, lg = lane >> 4;
+    f32x4 gram[4], qk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gram[j] = {0.f, 0.f, 0.f, 0.f};
+        qk[j] = {0.f, 0.f, 0.f, 0.f};
+        if (j <= wave) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const half8 ka = lds_half8(&Kh[wave * 16 + li][ks * 32 + lg * 8]);
+                const half8 qa = lds_half8(&Qh[wave * 16 + li][ks * 32 + lg * 8]);
+                const half8 kb = lds_half8(&Kh[j * 16 + li][ks * 32 + lg * 8]);
+                gram[j] = mfma16(ka, kb, gram[j]);
+                qk[j] = mfma16(qa, kb, qk[j]);
+            }
+        }
+    }
+
+    // normalised Q rows and K^T go to the workspace for the carry
+    if (qk_writer) {
+        uint16_t *qdst = p.qn + ((int64_t)chunk * Hk + kh) * C * DH;
+        uint16_t *kdst = p.knT + ((int64_t)chunk * Hk + kh) * DH * C;
+        for (int e = threadIdx.x; e < C * DH / 8; e += 256) {
+            const int t = e / (DH / 8), c8 = (e % (DH / 8)) * 8;
+            *reinterpret_cast<half8 *>(qdst + t * DH + c8) = lds_half8(&Qh[t][c8]);
+        }
+        for (int e = threadIdx.x; e < DH * C / 8; e += 256) {
+            const int dk = e / (C / 8), t8 = (e % (C / 8)) * 8;
+            half8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = Kh[t8 + i][dk];
+            *reinterpret_cast<half8 *>(kdst + dk * C + t8) = v;
+        }
+    }
+    __syncthreads();  // Kh / Qh are dead from here: X1 becomes A / T, X2 scratch
+
+    // -- A (strictly lower, f32) into X1; decayed, masked Q K^T to the workspace
+    {
+        uint16_t *aq = p.aqk + ((int64_t)chunk * Hv + h) * C * C;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = wave * 16 + lg * 4 + r, s = j * 16 + li;
+                const float dg = s <= t ? expf(G_s[t] - G_s[s]) : 0.f;
+                Am[t][s] = s < t ? beta_s[t] * dg * gram[j][r] : 0.f;
+                aq[t * C + s] = f32_to_f16_bits(dg * qk[j][r]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // -- T = (I + A)^-1 in place. (a) the four 16x16 diagonal blocks by forward
+    // substitution: wave 0, lane = (block, column).
+    if (wave == 0) {
+        const int b0 = (lane >> 4) * 16, c = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s)
+                acc += Am[b0 + r][b0 + s] * x[s];
+            x[r] = r < c ? 0.f : (r == c ? 1.f : -acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            Am[b0 + r][b0 + c] = x[r];
+    }
+    __syncthreads();
+    // (b) 32x32 diagonal halves: T10 = -T11 (A10 T00), waves 0 and 1 (blocks 1,0 and 3,2)
+    if (wave < 2) {
+        const int bi = (2 * wave + 1) * 16, bj = 2 * wave * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = mfma4(Am[bi + li][bj + ks * 4 + lg], Am[bj + ks * 4 + lg][bj + li], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Pm[wave * 16 + lg * 4 + r][li] = acc[r];
+    }
+    __syncthreads();
+    if (wave < 2) {
+        const int bi = (2 * wave + 1) * 16, bj = 2 * wave * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = mfma4(Am[bi + li][bi + ks * 4 + lg], Pm[wave * 16 + ks * 4 + lg][li], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Am[bi + lg * 4 + r][bj + li] = -acc[r];
+    }
+    __syncthreads();
+    // (c) lower-left 32x32: T_LL = -T_11 (A_LL T_00); wave = one 16x16 output tile
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            acc = mfma4(Am[32 + ti * 16 + li][ks * 4 + lg], Am[ks * 4 + lg][tj * 16 + li], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Pm[ti * 16 + lg * 4 + r][tj * 16 + li] = acc[r];
+    }
+    __syncthreads();
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            acc = mfma4(Am[32 + ti * 16 + li][32 + ks * 4 + lg], Pm[ks * 4 + lg][tj * 16 + li], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Am[32 + ti * 16 + lg * 4 + r][tj * 16 + li] = -acc[r];
+    }
+    __syncthreads();
+
+    // -- U = T (beta V) and W = T (beta gamma K): wave w owns token rows 16w..
+    {
+        half8 ta[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ta[ks][i] = (_Float16)Am[wave * 16 + li][ks * 32 + lg * 8 + i];
+        float *ud = p.umat + ((int64_t)chunk * Hv + h) * C * DH;
+        uint16_t *wd = p.wmat + ((int64_t)chunk * Hv + h) * C * DH;
+#pragma unroll
+        for (int nt = 0; nt < DH / 16; ++nt) {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u = mfma16(ta[ks], lds_half8(&VbT[nt * 16 + li][ks * 32 + lg * 8]), u);
+                w = mfma16(ta[ks], lds_half8(&KbT[nt * 16 + li][ks * 32 + lg * 8]), w);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = wave * 16 + lg * 4 + r;
+                ud[t * DH + nt * 16 + li] = u[r];
+                wd[t * DH + nt * 16 + li] = f32_to_f16_bits(w[r]);
+            }
+        }
+    }
+    if (threadIdx.x < C)
+        p.gcum[((int64_t)chunk * Hv + h) * C + threadIdx.x] = G_s[threadIdx.x];
+}
+
+// ---------------------------------------------------------------- 3. carry
+
+// One chunk's operands for one wave of the carry, as loaded from the workspace.
+struct CarryOps {
+    half8 w[4], q[4], aq[2], kt[2][2];
+    float u[4], g[4], gl;
+};
+
+__device__ __forceinline__ void load_carry_ops(CarryOps &o, const PrefillParams &p, int chunk,
+                                               int h, int kh, int wave, int li, int lg, int dv0)
+{
+    const int Hv = p.hc.Hv, Hk = p.hc.Hk;
+    const uint16_t *wsrc = p.wmat + ((int64_t)chunk * Hv + h) * C * DH + (wave * 16 + li) * DH + lg * 8;
+    const uint16_t *qsrc = p.qn + ((int64_t)chunk * Hk + kh) * C * DH + (wave * 16 + li) * DH + lg * 8;
+    const uint16_t *asrc = p.aqk + ((int64_t)chunk * Hv + h) * C * C + (wave * 16 + li) * C + lg * 8;
+    const uint16_t *ksrc = p.knT + ((int64_t)chunk * Hk + kh) * DH * C + (wave * 32 + li) * C + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        o.w[ks] = glb_half8(wsrc + ks * 32);
+        o.q[ks] = glb_half8(qsrc + ks * 32);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        o.aq[ks] = glb_half8(asrc + ks * 32);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            o.kt[nt][ks] = glb_half8(ksrc + nt * 16 * C + ks * 32);
+    }
+    const float *usrc = p.umat + ((int64_t)chunk * Hv + h) * C * DH;
+    const float *gsrc = p.gcum + ((int64_t)chunk * Hv + h) * C;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = wave * 16 + lg * 4 + r;
+        o.u[r] = usrc[t * DH + dv0 + li];
+        o.g[r] = gsrc[t];
+    }
+    o.gl = gsrc[C - 1];
+}
+
+__global__ __launch_bounds__(256) void carry_kernel(PrefillParams p)
+{
+    __shared__ __attribute__((aligned(16))) _Float16 Sh[DT][KP];     // f16 copy of the state slice
+    __shared__ __attribute__((aligned(16))) _Float16 DTl[DT][TP];    // D^T (for Aqk D)
+    __shared__ __attribute__((aligned(16))) _Float16 DsH[DT][TP];    // (decayed D)^T, hi part
+    __shared__ __attribute__((aligned(16))) _Float16 DsL[DT][TP];    // (decayed D)^T, lo part
+
+    const HeadCfg &hc = p.hc;
+    const int Hv = hc.Hv;
+    constexpr int NT = DH / DT;  // dv slices per head
+    // XCD-aware order: the NT slices of one (sequence, head) share id % 8, so
+    // they run on one XCD and share its L2 for the chunk operands.
+    const int id = blockIdx.x;
+    const int group = (id & 7) + 8 * (id / (8 * NT));
+    const int slice = (id >> 3) % NT;
+    if (group >= p.N * Hv)
+        return;
+    const int seq = group / Hv, h = group % Hv;
+    const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
+    const int dv0 = slice * DT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int start = p.cu[seq];
+    const int len = p.cu[seq + 1] - start;
+    const int nch = (len + C - 1) / C;
+    if (nch == 0)
+        return;  // empty sequence: state untouched
+    const int c0 = p.seq_chunk0[seq];
+
+    // state slice: wave w holds dk columns 32w .. 32w+31 as two 16x16 tiles
+    float *Sg = p.state + ((int64_t)seq * Hv + h) * DH * DH;
+    f32x4 S[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int dv = dv0 + lg * 4 + r, dk = wave * 32 + nt * 16 + li;
+            S[nt][r] = Sg[(int64_t)dv * DH + dk];
+            Sh[lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
+        }
+
+    CarryOps cur, nxt;
+    load_carry_ops(cur, p, c0, h, kh, wave, li, lg, dv0);
+    const bool norm_out = hc.flags & F_GATED_NORM;
+    __syncthreads();
+
+    for (int ci = 0; ci < nch; ++ci) {
+        const int chunk = c0 + ci;
+        const int tok0 = start + ci * C;
+        const int n = min(C, len - ci * C);
+        if (ci + 1 < nch)
+            load_carry_ops(nxt, p, chunk + 1, h, kh, wave, li, lg, dv0);
+
+        // P = W S0^T and QS = Q S0^T for token rows 16w..16w+15 (B operand: S0 rows)
+        f32x4 P = {0.f, 0.f, 0.f, 0.f}, QS = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8 sb = lds_half8(&Sh[li][ks * 32 + lg * 8]);
+            P = mfma16(cur.w[ks], sb, P);
+            QS = mfma16(cur.q[ks], sb, QS);
+        }
+        // D = U - P; decayed D for the state update, as an f16 hi + lo pair
+        f32x4 O;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = wave * 16 + lg * 4 + r;
+            const float d = cur.u[r] - P[r];
+            const float ds = d * expf(cur.gl - cur.g[r]);
+            const _Float16 dh = (_Float16)ds;
+            DTl[li][t] = (_Float16)d;
+            DsH[li][t] = dh;
+            DsL[li][t] = (_Float16)(ds - (float)dh);
+            O[r] = expf(cur.g[r]) * QS[r];
+        }
+        __syncthreads();
+
+        // O = scale (gamma QS + Aqk D)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            O = mfma16(cur.aq[ks], lds_half8(&DTl[li][ks * 32 + lg * 8]), O);
+        // S_n = gamma_{n-1} S0 + D~^T K, D~ = hi + lo
+        const float gn = expf(cur.gl);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            S[nt] *= gn;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                S[nt] = mfma16(lds_half8(&DsH[li][ks * 32 + lg * 8]), cur.kt[nt][ks], S[nt]);
+                S[nt] = mfma16(lds_half8(&DsL[li][ks * 32 + lg * 8]), cur.kt[nt][ks], S[nt]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = wave * 16 + lg * 4 + r;
+            if (t < n) {
+                const int64_t row = (int64_t)(tok0 + t) * Hv + h;
+                if (norm_out)
+                    p.onorm[row * DH + dv0 + li] = hc.scale * O[r];
+                else
+                    store_act(p.out, row * DH + dv0 + li, p.out_dt, hc.scale * O[r]);
+            }
+        }
+        __syncthreads();  // every wave has read Sh and D for this chunk
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sh[lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
+        __syncthreads();
+        if (ci + 1 < nch)
+            cur = nxt;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int dv = dv0 + lg * 4 + r, dk = wave * 32 + nt * 16 + li;
+            Sg[(int64_t)dv * DH + dk] = S[nt][r];
+        }
+}
+
+// ---------------------------------------------------------------- 4. gated norm
+
+__global__ __launch_bounds__(256) void norm_kernel(PrefillParams p)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, v-head)
+    if (row >= (int64_t)p.total * p.hc.Hv)
+        return;
+    const int lane = threadIdx.x & 63;
+    const float *o = p.onorm + row * DH;
+    const float o0 = o[lane], o1 = o[lane + 64];
+    const float ss = group_sum<64>(o0 * o0 + o1 * o1);
+    const float inv = rsqrtf(ss / (float)DH + p.hc.norm_eps);
+    const float z0 = load_act(p.in.z, row * DH + lane, p.in.z_dt);
+    const float z1 = load_act(p.in.z, row * DH + lane + 64, p.in.z_dt);
+    store_act(p.out, row * DH + lane, p.out_dt, o0 * inv * p.in.norm_w[lane] * silu_f(z0));
+    store_act(p.out, row * DH + lane + 64, p.out_dt, o1 * inv * p.in.norm_w[lane + 64] * silu_f(z1));
+}
+
+}  // namespace
+
+bool prefill_supported(int dk, int dv) { return dk == DH && dv == DH; }
+
+size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
+                               int64_t total_tokens, bool norm)
+{
+    (void)dk;
+    (void)dv;
+    return ws_layout(Hk, Hv, max_chunks, N, total_tokens, norm).total;
+}
+
+void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
+{
+    const WsLayout L = ws_layout(p.hc.Hk, p.hc.Hv, max_chunks, p.N, p.total,
+                                 (p.hc.flags & F_GATED_NORM) != 0);
+    unsigned char *b = static_cast<unsigned char *>(ws);
+    p.chunk_seq = reinterpret_cast<int32_t *>(b + L.chunk_seq);
+    p.chunk_start = reinterpret_cast<int32_t *>(b + L.chunk_start);
+    p.chunk_len = reinterpret_cast<int32_t *>(b + L.chunk_len);
+    p.seq_chunk0 = reinterpret_cast<int32_t *>(b + L.seq_chunk0);
+    p.qn = reinterpret_cast<uint16_t *>(b + L.qn);
+    p.knT = reinterpret_cast<uint16_t *>(b + L.knT);
+    p.wmat = reinterpret_cast<uint16_t *>(b + L.wmat);
+    p.umat = reinterpret_cast<float *>(b + L.umat);
+    p.aqk = reinterpret_cast<uint16_t *>(b + L.aqk);
+    p.gcum = reinterpret_cast<float *>(b + L.gcum);
+    p.onorm = reinterpret_cast<float *>(b + L.onorm);
+}
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
+{
+    if (p.num_chunks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
+    const dim3 pgrid((unsigned)((int64_t)p.num_chunks * p.hc.Hv));
+    switch (p.in.qkv_dt) {
+    case DT_F32: hipLaunchKernelGGL((prep_kernel<DT_F32>), pgrid, dim3(256), 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
+    }
+    const int64_t groups = (int64_t)p.N * p.hc.Hv;
+    const int64_t cblocks = (groups + 7) / 8 * 8 * (DH / DT);
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)cblocks), dim3(256), 0, s, p);
+    if (p.hc.flags & F_GATED_NORM) {
+        const int64_t rows = (int64_t)p.total * p.hc.Hv;
+        hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
 
 }  // namespace gdn
