@@ -148,6 +148,74 @@ def decode_bench(args, torch, ops, synth):
     return res
 
 
+def prefill_bench(torch, ops, synth, calls=20, warmup=5):
+    """Chunked prefill, B=1, T=4096, Hk=16, Hv=32, d=128, grouped map, bf16 N(0,1)
+    inputs, raw gates with A_log ~ U[-2,0], q/k L2-normalised in-op, zero initial
+    state, f32 core output (no gated norm)."""
+    dev = torch.device("cuda:0")
+    T, Hk, Hv, d = 4096, 16, 32, 128
+    P = synth.prefill(seed=3, lengths=[T], Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.GROUPED)
+    g = lambda t: t.reshape(T, -1).to(dev).contiguous()  # noqa: E731
+    q, k, v, a, b = g(P["q"]), g(P["k"]), g(P["v"]), g(P["a"]), g(P["b"])
+    state0 = P["state"].to(dev).contiguous()
+    state = state0.clone()
+    out = torch.empty((T, Hv, d), dtype=torch.float32, device=dev)
+    cu_h = P["cu_seqlens"].contiguous()
+    cu_d = cu_h.to(dev)
+    need = ops.prefill_workspace_bytes(Hk=Hk, Hv=Hv, dk=d, dv=d, num_seqs=1, total_tokens=T)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    call = ops.prepare_prefill_chunked(q, k, v, state, cu_d, cu_h, out, ws, Hk=Hk, Hv=Hv, dk=d,
+                                       dv=d, head_map=synth.GROUPED, a=a, b=b,
+                                       decay_param=P["A_log"].to(dev),
+                                       dt_bias=P["dt_bias"].to(dev))
+    for _ in range(warmup):
+        state.copy_(state0)
+        call.launch()
+    times = []
+    for _ in range(calls):
+        state.copy_(state0)  # every call starts from the zero state (outside the timed span)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call.launch()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    C = 64
+    chunks = T // C
+    # algorithmic MFMA work of the chunked form, per (chunk, v-head): U, W (2 C^2 d
+    # each), W S^T, Q S^T, D^T K (2 C d^2 each), Aqk D (2 C^2 d); per (chunk, k-head):
+    # K K^T and Q K^T (2 C^2 d each)
+    flops = chunks * (Hv * (3 * 2 * C * C * d + 3 * 2 * C * d * d) + Hk * 2 * 2 * C * C * d)
+    # HBM bytes: bf16 q, k, v, a, b in; f32 output; the state read and written once
+    hbm = T * (2 * Hk * d + Hv * d + 2 * Hv) * 2 + T * Hv * d * 4 + 2 * Hv * d * d * 4
+    t = ms * 1e-3
+    return dict(workload="chunked prefill: B=1, T=4096, C=64, Hk=16, Hv=32, dk=dv=128, grouped "
+                         "map, bf16 N(0,1) inputs, q/k L2-normalised, raw gates, zero initial "
+                         "state, f32 core output",
+                tokens_per_s=T / t, ms_per_call=ms, calls=calls, unit="tokens/s",
+                mfma_flops=flops, mfma_util=flops / t / (MFMA_F16_PEAK_TFLOPS * 1e12),
+                roofline=dict(bound="hbm", achieved=hbm / t / 1e9, peak=HBM_PEAK_GBS,
+                              unit="GB/s", frac=hbm / t / 1e9 / HBM_PEAK_GBS, bytes=hbm))
+
+
+def counter_pass(torch, ops, synth, steps=10, copy_mib=256):
+    """For HBM-byte counters: `steps` decode steps of the headline workload, then
+    `steps` copies of copy_mib MiB (read and written once each: 2 * copy_mib MiB
+    of traffic per dispatch), whose counter readings calibrate the decode's."""
+    args = argparse.Namespace(warmup=2, steps=steps)
+    decode_bench(args, torch, ops, synth)
+    n = copy_mib * 2 ** 20 // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] counter pass: {steps} decode steps, {steps} copies of {copy_mib} MiB",
+          file=sys.stderr, flush=True)
+
+
 def cpu_baseline(seconds):
     """The f64 CPU oracle on the decode workload, B=64, for >= `seconds` of work."""
     import numpy as np
@@ -185,6 +253,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc: a few decode steps, then a plain "
+                         "256 MiB device copy of known size (the counters' calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -201,6 +273,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.counter_pass:
+        counter_pass(torch, ops, synth)
+        return
     print(f"[bench] decode B=64: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     dec = decode_bench(args, torch, ops, synth)
@@ -212,6 +287,12 @@ def main():
                 data="synthetic", config=dec["config"],
                 pct_hbm_peak=round(100 * dec["value"] / HBM_PEAK_GBS, 2),
                 roofline=dec["roofline"], rotating=dec["rotating"])
+    if not args.no_prefill:
+        print("[bench] prefill T=4096", file=sys.stderr, flush=True)
+        pre = prefill_bench(torch, ops, synth)
+        print(f"[bench] prefill {pre['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+              f"{pre['ms_per_call'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+        line["prefill"] = pre
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

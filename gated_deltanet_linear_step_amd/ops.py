@@ -302,3 +302,26 @@ def prepare_decode_step(q, k, v, state, out, *, Hk, Hv, dk, dv, head_map, batch,
             _ptr(state_slots), state.shape[0], _dt(out), _ptr(out), _stream(stream))
     return PreparedCall(load().gdn_decode_step, args, "gdn_decode_step",
                         keep + [dims, inp, state, out, state_slots])
+
+
+def prepare_prefill_chunked(q, k, v, state, cu_seqlens_dev, cu_seqlens_host, out, workspace, *,
+                            Hk, Hv, dk, dv, head_map, a=None, b=None, decay_param=None,
+                            dt_bias=None, g=None, beta=None, z=None, norm_weight=None,
+                            l2norm_qk=True, decay=DECAY_LOG_RATE, scale=0.0,
+                            stream=None) -> PreparedCall:
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    if cu_seqlens_host.device.type != "cpu" or cu_seqlens_host.dtype != torch.int32:
+        raise ValueError("cu_seqlens_host must be a CPU int32 tensor")
+    N = cu_seqlens_host.numel() - 1
+    total = int(cu_seqlens_host[-1])
+    args = (ctypes.byref(dims), N, ctypes.c_void_p(cu_seqlens_host.data_ptr()),
+            _ptr(cu_seqlens_dev), total, ctypes.byref(inp), _ptr(state), _dt(out), _ptr(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(load().gdn_prefill_chunked, args, "gdn_prefill_chunked",
+                        keep + [dims, inp, state, out, workspace, cu_seqlens_dev,
+                                cu_seqlens_host])
