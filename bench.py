@@ -12,7 +12,8 @@ Metric: decode state GB/s = 2 * B * Hv * dv * dk * 4 bytes (the fp32 state read
 and written once) / step time, the definition of the ferrox-core gdn.rs
 throughput probe. Also reported on the same JSON line:
   * roofline: the decode kernel's algorithmic bytes per launch / its average
-    duration (HIP events around every decode launch in the timed region), against
+    duration (one HIP event pair around K back-to-back decode launches, timed
+    right after the K steps), against
     the 8 TB/s HBM peak; traffic from the committed rocprofv3 FETCH/WRITE counter
     summary when it was taken on the current kernel source, else null;
   * rotating: the same step cycling through 4 independent state sets (537 MB,
@@ -80,30 +81,34 @@ def decode_bench(args, torch, ops, synth):
         sets.append(S)
     main = sets[0]
 
-    def step(S, ev=None):
+    def step(S):
         S["conv"].launch()
-        if ev is not None:
-            ev[0].record()
         S["dec"].launch()
-        if ev is not None:
-            ev[1].record()
 
     for _ in range(args.warmup):
         step(main)
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    # timed region 1 (the metric): K whole steps, one event pair around them
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t0.record()
     for i in range(K):
-        step(main, evs[i])
+        step(main)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t0.elapsed_time(t1) / K
-    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    # timed region 2 (the roofline): K decode launches back to back on the same
+    # stream, one event pair around them -> the decode kernel's average duration
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record()
+    for i in range(K):
+        main["dec"].launch()
+    d1.record()
+    torch.cuda.synchronize()
+    dec_ms = d0.elapsed_time(d1) / K
 
     state_bytes = 2 * B * Hv * d * d * 4
     # decode kernel algorithmic bytes: state r+w, q/k/v read (f32 conv output),
