@@ -204,42 +204,63 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     }
     __syncthreads();
 
-    // -- rows of k, q, v: wave w loads tokens 16w .. 16w+15, 32 lanes per row
+    // -- rows of k and q: wave w loads tokens 16w .. 16w+15, 32 lanes per row;
+    // rows past the chunk's end re-read its last row and are zeroed after.
     {
         const int sub = lane >> 5, c4 = (lane & 31) * 4;
+        Raw4<QT> kr[8], qr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = wave * 16 + 2 * i + sub;
-            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), qq = kk, vv = kk;
-            if (t < n) {
-                const int64_t r = tok0 + t;
-                kk = load_act4_t<QT>(in.k, r * in.k_stride + (int64_t)kh * DH + c4);
-                qq = load_act4_t<QT>(in.q, r * in.q_stride + (int64_t)kh * DH + c4);
-                vv.x = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4);
-                vv.y = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4 + 1);
-                vv.z = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4 + 2);
-                vv.w = load_act_t<QT>(in.v, r * in.v_stride + (int64_t)h * DH + c4 + 3);
-            }
+            const int64_t r = tok0 + min(t, n - 1);
+            kr[i] = load_raw4<QT>(in.k, r * in.k_stride + (int64_t)kh * DH + c4);
+            qr[i] = load_raw4<QT>(in.q, r * in.q_stride + (int64_t)kh * DH + c4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = wave * 16 + 2 * i + sub;
+            float4 kk = raw4_to_f32<QT>(kr[i]), qq = raw4_to_f32<QT>(qr[i]);
             if (flags & F_L2NORM) {
                 const float ik = rsqrtf(group_sum<32>(dot4(kk, kk)) + hc.l2_eps);
                 const float iq = rsqrtf(group_sum<32>(dot4(qq, qq)) + hc.l2_eps);
                 kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
                 qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
             }
-            Kh[t][c4] = (_Float16)kk.x; Kh[t][c4 + 1] = (_Float16)kk.y;
-            Kh[t][c4 + 2] = (_Float16)kk.z; Kh[t][c4 + 3] = (_Float16)kk.w;
-            Qh[t][c4] = (_Float16)qq.x; Qh[t][c4 + 1] = (_Float16)qq.y;
-            Qh[t][c4 + 2] = (_Float16)qq.z; Qh[t][c4 + 3] = (_Float16)qq.w;
-            const float bt = beta_s[t];
-            const float bg = bt * expf(G_s[t]);
-            VbT[c4][t] = (_Float16)(bt * vv.x); VbT[c4 + 1][t] = (_Float16)(bt * vv.y);
-            VbT[c4 + 2][t] = (_Float16)(bt * vv.z); VbT[c4 + 3][t] = (_Float16)(bt * vv.w);
-            // the f16-rounded normalised k, scaled: the same K the carry multiplies
-            KbT[c4][t] = (_Float16)(bg * (float)(_Float16)kk.x);
-            KbT[c4 + 1][t] = (_Float16)(bg * (float)(_Float16)kk.y);
-            KbT[c4 + 2][t] = (_Float16)(bg * (float)(_Float16)kk.z);
-            KbT[c4 + 3][t] = (_Float16)(bg * (float)(_Float16)kk.w);
+            const float keep = t < n ? 1.f : 0.f;
+            typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+            const half4 kh4 = {(_Float16)(keep * kk.x), (_Float16)(keep * kk.y),
+                               (_Float16)(keep * kk.z), (_Float16)(keep * kk.w)};
+            const half4 qh4 = {(_Float16)(keep * qq.x), (_Float16)(keep * qq.y),
+                               (_Float16)(keep * qq.z), (_Float16)(keep * qq.w)};
+            *reinterpret_cast<half4 *>(&Kh[t][c4]) = kh4;
+            *reinterpret_cast<half4 *>(&Qh[t][c4]) = qh4;
         }
+    }
+    __syncthreads();
+
+    // -- transposed tiles, one (dim, 8-token octet) item per 16-byte LDS write:
+    // beta v from the input (lanes along dim: coalesced), beta gamma k from the
+    // f16 rows just written (the same rounded K the gram and the carry use).
+#pragma unroll
+    for (int it = 0; it < (DH * C / 8) / 256; ++it) {
+        const int e = it * 256 + threadIdx.x;
+        const int j = e % DH, o = e / DH;
+        half8 vb, kb;
+        uint32_t vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = tok0 + min(o * 8 + i, n - 1);
+            vr[i] = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DH + j);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = o * 8 + i;
+            const float bt = beta_s[t];  // 0 for tokens past the chunk's end
+            vb[i] = (_Float16)(bt * raw1_to_f32<QT>(vr[i]));
+            kb[i] = (_Float16)(bt * __expf(G_s[t]) * (float)Kh[t][j]);
+        }
+        *reinterpret_cast<half8 *>(&VbT[j][o * 8]) = vb;
+        *reinterpret_cast<half8 *>(&KbT[j][o * 8]) = kb;
     }
     __syncthreads();
 
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             *reinterpret_cast<half8 *>(qdst + t * DH + c8) = lds_half8(&Qh[t][c8]);
         }
         for (int e = threadIdx.x; e < DH * C / 8; e += 256) {
-            const int dk = e / (C / 8), t8 = (e % (C / 8)) * 8;
+            const int dk = e % DH, t8 = (e / DH) * 8;
             half8 v;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -289,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = wave * 16 + lg * 4 + r, s = j * 16 + li;
-                const float dg = s <= t ? expf(G_s[t] - G_s[s]) : 0.f;
+                const float dg = s <= t ? __expf(G_s[t] - G_s[s]) : 0.f;
                 Am[t][s] = s < t ? beta_s[t] * dg * gram[j][r] : 0.f;
                 aq[t * C + s] = f32_to_f16_bits(dg * qk[j][r]);
             }
@@ -431,9 +452,26 @@ __device__ __forceinline__ void load_carry_ops(CarryOps &o, const PrefillParams 
     o.gl = gsrc[C - 1];
 }
 
-__global__ __launch_bounds__(256) void carry_kernel(PrefillParams p)
+// OUT: the output's dtype, or kOutNorm for the f32 buffer the gated norm reads
+constexpr int kOutNorm = 3;
+
+template <int OUT>
+__device__ __forceinline__ void store_out(const PrefillParams &p, int64_t idx, float v)
 {
-    __shared__ __attribute__((aligned(16))) _Float16 Sh[DT][KP];     // f16 copy of the state slice
+    if constexpr (OUT == kOutNorm)
+        p.onorm[idx] = v;
+    else if constexpr (OUT == DT_F32)
+        static_cast<float *>(p.out)[idx] = v;
+    else if constexpr (OUT == DT_BF16)
+        static_cast<uint16_t *>(p.out)[idx] = f32_to_bf16_bits(v);
+    else
+        static_cast<uint16_t *>(p.out)[idx] = f32_to_f16_bits(v);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256, 1) void carry_kernel(PrefillParams p)
+{
+    __shared__ __attribute__((aligned(16))) _Float16 Sh[2][DT][KP];  // f16 state slice, ping-pong
     __shared__ __attribute__((aligned(16))) _Float16 DTl[DT][TP];    // D^T (for Aqk D)
     __shared__ __attribute__((aligned(16))) _Float16 DsH[DT][TP];    // (decayed D)^T, hi part
     __shared__ __attribute__((aligned(16))) _Float16 DsL[DT][TP];    // (decayed D)^T, lo part
@@ -459,6 +497,7 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillParams p)
     if (nch == 0)
         return;  // empty sequence: state untouched
     const int c0 = p.seq_chunk0[seq];
+    const int clast = c0 + nch - 1;
 
     // state slice: wave w holds dk columns 32w .. 32w+31 as two 16x16 tiles
     float *Sg = p.state + ((int64_t)seq * Hv + h) * DH * DH;
@@ -469,79 +508,85 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillParams p)
         for (int r = 0; r < 4; ++r) {
             const int dv = dv0 + lg * 4 + r, dk = wave * 32 + nt * 16 + li;
             S[nt][r] = Sg[(int64_t)dv * DH + dk];
-            Sh[lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
+            Sh[0][lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
         }
-
-    CarryOps cur, nxt;
-    load_carry_ops(cur, p, c0, h, kh, wave, li, lg, dv0);
-    const bool norm_out = hc.flags & F_GATED_NORM;
     __syncthreads();
 
-    for (int ci = 0; ci < nch; ++ci) {
-        const int chunk = c0 + ci;
+    // One chunk with operands `o`, reading the state copy Sh[ci & 1] and leaving
+    // the new one in Sh[(ci + 1) & 1]: two barriers per chunk.
+    auto process = [&](const CarryOps &o, int ci) {
         const int tok0 = start + ci * C;
         const int n = min(C, len - ci * C);
-        if (ci + 1 < nch)
-            load_carry_ops(nxt, p, chunk + 1, h, kh, wave, li, lg, dv0);
-
+        const int sb = ci & 1;
         // P = W S0^T and QS = Q S0^T for token rows 16w..16w+15 (B operand: S0 rows)
         f32x4 P = {0.f, 0.f, 0.f, 0.f}, QS = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const half8 sb = lds_half8(&Sh[li][ks * 32 + lg * 8]);
-            P = mfma16(cur.w[ks], sb, P);
-            QS = mfma16(cur.q[ks], sb, QS);
+            const half8 b = lds_half8(&Sh[sb][li][ks * 32 + lg * 8]);
+            P = mfma16(o.w[ks], b, P);
+            QS = mfma16(o.q[ks], b, QS);
         }
         // D = U - P; decayed D for the state update, as an f16 hi + lo pair
         f32x4 O;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = wave * 16 + lg * 4 + r;
-            const float d = cur.u[r] - P[r];
-            const float ds = d * expf(cur.gl - cur.g[r]);
+            const float d = o.u[r] - P[r];
+            const float ds = d * __expf(o.gl - o.g[r]);
             const _Float16 dh = (_Float16)ds;
             DTl[li][t] = (_Float16)d;
             DsH[li][t] = dh;
             DsL[li][t] = (_Float16)(ds - (float)dh);
-            O[r] = expf(cur.g[r]) * QS[r];
+            O[r] = __expf(o.g[r]) * QS[r];
         }
         __syncthreads();
-
         // O = scale (gamma QS + Aqk D)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            O = mfma16(cur.aq[ks], lds_half8(&DTl[li][ks * 32 + lg * 8]), O);
+            O = mfma16(o.aq[ks], lds_half8(&DTl[li][ks * 32 + lg * 8]), O);
         // S_n = gamma_{n-1} S0 + D~^T K, D~ = hi + lo
-        const float gn = expf(cur.gl);
+        const float gn = __expf(o.gl);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             S[nt] *= gn;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                S[nt] = mfma16(lds_half8(&DsH[li][ks * 32 + lg * 8]), cur.kt[nt][ks], S[nt]);
-                S[nt] = mfma16(lds_half8(&DsL[li][ks * 32 + lg * 8]), cur.kt[nt][ks], S[nt]);
+                S[nt] = mfma16(lds_half8(&DsH[li][ks * 32 + lg * 8]), o.kt[nt][ks], S[nt]);
+                S[nt] = mfma16(lds_half8(&DsL[li][ks * 32 + lg * 8]), o.kt[nt][ks], S[nt]);
             }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = wave * 16 + lg * 4 + r;
-            if (t < n) {
-                const int64_t row = (int64_t)(tok0 + t) * Hv + h;
-                if (norm_out)
-                    p.onorm[row * DH + dv0 + li] = hc.scale * O[r];
-                else
-                    store_act(p.out, row * DH + dv0 + li, p.out_dt, hc.scale * O[r]);
-            }
+            if (t < n)
+                store_out<OUT>(p, ((int64_t)(tok0 + t) * Hv + h) * DH + dv0 + li, hc.scale * O[r]);
         }
-        __syncthreads();  // every wave has read Sh and D for this chunk
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Sh[lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
-        __syncthreads();
-        if (ci + 1 < nch)
-            cur = nxt;
+                Sh[sb ^ 1][lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
+        __syncthreads();  // the new state copy is complete; D may be overwritten
+    };
+
+    // Operands are prefetched two chunks ahead through three register buffers
+    // (indices past the sequence's last chunk re-load the last one, harmlessly).
+    CarryOps A, B, Cb;
+    load_carry_ops(A, p, c0, h, kh, wave, li, lg, dv0);
+    load_carry_ops(B, p, min(c0 + 1, clast), h, kh, wave, li, lg, dv0);
+    for (int ci = 0;;) {
+        load_carry_ops(Cb, p, min(c0 + ci + 2, clast), h, kh, wave, li, lg, dv0);
+        process(A, ci);
+        if (++ci == nch)
+            break;
+        load_carry_ops(A, p, min(c0 + ci + 2, clast), h, kh, wave, li, lg, dv0);
+        process(B, ci);
+        if (++ci == nch)
+            break;
+        load_carry_ops(B, p, min(c0 + ci + 2, clast), h, kh, wave, li, lg, dv0);
+        process(Cb, ci);
+        if (++ci == nch)
+            break;
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -612,8 +657,14 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
     default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
     }
     const int64_t groups = (int64_t)p.N * p.hc.Hv;
-    const int64_t cblocks = (groups + 7) / 8 * 8 * (DH / DT);
-    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)cblocks), dim3(256), 0, s, p);
+    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / DT)));
+    const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
+    switch (omode) {
+    case kOutNorm: hipLaunchKernelGGL((carry_kernel<kOutNorm>), cgrid, dim3(256), 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((carry_kernel<DT_F32>), cgrid, dim3(256), 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((carry_kernel<DT_F16>), cgrid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((carry_kernel<DT_BF16>), cgrid, dim3(256), 0, s, p); break;
+    }
     if (p.hc.flags & F_GATED_NORM) {
         const int64_t rows = (int64_t)p.total * p.hc.Hv;
         hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
