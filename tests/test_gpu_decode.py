@@ -292,3 +292,40 @@ def test_conv_update_one_token_per_sequence(act, y_dtype, C):
         bound = 1e-5 if y_dtype == torch.float32 else ulp16(yo, y_dtype) + 1e-5
         assert np.all(err <= bound)
         assert maxabs(f64(cs_d[i]), so) == 0.0
+
+
+def test_negative_rate_decay_matches_oracle():
+    # decay parameter given as -exp(A_log) (the NegativeRate parameterisation)
+    B, T = 3, 2
+    W = to_dev(synth.decode_batch(seed=31, B=B, T=T, Hk=2, Hv=4, head_map=synth.TILED))
+    neg = -torch.exp(W["A_log"])
+    Hk, Hv, d = 2, 4, 128
+    QK = Hk * d
+    y = ops.conv_update(W["x_d"], W["conv_w_d"], W["conv_state_d"])
+    out = ops.decode_step(y[:, :QK], y[:, QK:2 * QK], y[:, 2 * QK:], W["state_d"], Hk=Hk, Hv=Hv,
+                          dk=d, dv=d, head_map=synth.TILED, batch=B, tokens_per_seq=T,
+                          a=W["a_d"], b=W["b_d"], decay_param=neg.to(DEV),
+                          dt_bias=W["dt_bias_d"], z=W["z_d"], norm_weight=W["norm_w_d"],
+                          decay=ops.DECAY_NEGATIVE_RATE)
+    torch.cuda.synchronize()
+    yo, cs, S = oracle.batch(B=B, T=T, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED,
+                             S0=f64(W["state"]), a=f64(W["a"]), b=f64(W["b"]),
+                             decay_param=f64(neg), dt_bias=f64(W["dt_bias"]), z=f64(W["z"]),
+                             norm_w=f64(W["norm_w"]), x=f64(W["x"]), conv_w=f64(W["conv_w"]),
+                             conv_state=f64(W["conv_state"]), nthreads=8,
+                             decay_kind=oracle.DECAY_NEGATIVE_RATE)
+    assert maxabs(f64(out).reshape(yo.shape), yo) <= TOL
+    assert maxabs(f64(W["state_d"]), S) <= TOL
+
+
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_multi_token_verify_decode_b64(T):
+    # several tokens per sequence in one call: the state is read and written once
+    B = 64
+    W = to_dev(synth.decode_batch(seed=40 + T, B=B, T=T, head_map=synth.TILED))
+    out = run_layer(W, T=T, B=B)
+    torch.cuda.synchronize()
+    y, cs, S = oracle_layer(W, B=B, T=T)
+    assert maxabs(f64(out).reshape(y.shape), y) <= TOL
+    assert maxabs(f64(W["state_d"]), S) <= TOL
+    assert maxabs(f64(W["conv_state_d"]), cs) == 0.0
