@@ -66,10 +66,21 @@ __device__ __forceinline__ half8 lds_half8(const _Float16 *p)
     return *reinterpret_cast<const half8 *>(p);
 }
 
-__device__ __forceinline__ half8 glb_half8(const uint16_t *p)
+// The carry feeds MFMA outputs straight back in as MFMA operands. A 16x16
+// output tile leaves lane l holding rows 4(l/16) .. 4(l/16)+3 of column l%16;
+// two such tiles (rows r and r+16) make up the 8 k-values one lane supplies to
+// a 16x16x32 product. Every matrix contracted against them is therefore stored
+// with each 32-wide block of the contracted index reordered so that slot
+// 8g + i holds index 4g + i (i < 4) or 16 + 4g + (i - 4) (i >= 4).
+__host__ __device__ constexpr int perm_pos(int c)  // slot of index c within its 32-block
 {
-    return *reinterpret_cast<const half8 *>(p);
+    return (c & ~31) | (8 * ((c & 15) >> 2) + (c & 3) + 4 * ((c >> 4) & 1));
 }
+__host__ __device__ constexpr int perm_idx(int p)  // index held by slot p
+{
+    return (p & ~31) | (4 * ((p >> 3) & 3) + (p & 3) + 16 * ((p >> 2) & 1));
+}
+static_assert(perm_idx(perm_pos(21)) == 21 && perm_pos(perm_idx(13)) == 13, "permutation");
 
 // ---------------------------------------------------------------- workspace
 
@@ -97,7 +108,7 @@ WsLayout ws_layout(int Hk, int Hv, int64_t MC, int N, int64_t total_tokens, bool
     L.wmat = take(sizeof(uint16_t) * MC * Hv * C * DH);
     L.umat = take(sizeof(float) * MC * Hv * C * DH);
     L.aqk = take(sizeof(uint16_t) * MC * Hv * C * C);
-    L.gcum = take(sizeof(float) * MC * Hv * C);
+    L.gcum = take(sizeof(float) * MC * Hv * 2 * C);
     L.onorm = norm ? take(sizeof(float) * (size_t)total_tokens * Hv * DH) : off;
     L.total = off;
     return L;
@@ -289,14 +300,18 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
         uint16_t *kdst = p.knT + ((int64_t)chunk * Hk + kh) * DH * C;
         for (int e = threadIdx.x; e < C * DH / 8; e += 256) {
             const int t = e / (DH / 8), c8 = (e % (DH / 8)) * 8;
-            *reinterpret_cast<half8 *>(qdst + t * DH + c8) = lds_half8(&Qh[t][c8]);
+            half8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = Qh[t][perm_idx(c8 + i)];
+            *reinterpret_cast<half8 *>(qdst + t * DH + c8) = v;
         }
         for (int e = threadIdx.x; e < DH * C / 8; e += 256) {
             const int dk = e % DH, t8 = (e / DH) * 8;
             half8 v;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                v[i] = Kh[t8 + i][dk];
+                v[i] = Kh[perm_idx(t8 + i)][dk];
             *reinterpret_cast<half8 *>(kdst + dk * C + t8) = v;
         }
     }
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
                 const int t = wave * 16 + lg * 4 + r, s = j * 16 + li;
                 const float dg = s <= t ? __expf(G_s[t] - G_s[s]) : 0.f;
                 Am[t][s] = s < t ? beta_s[t] * dg * gram[j][r] : 0.f;
-                aq[t * C + s] = f32_to_f16_bits(dg * qk[j][r]);
+                aq[t * C + perm_pos(s)] = f32_to_f16_bits(dg * qk[j][r]);
             }
         }
     }
@@ -405,52 +420,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             for (int r = 0; r < 4; ++r) {
                 const int t = wave * 16 + lg * 4 + r;
                 ud[t * DH + nt * 16 + li] = u[r];
-                wd[t * DH + nt * 16 + li] = f32_to_f16_bits(w[r]);
+                wd[t * DH + perm_pos(nt * 16 + li)] = f32_to_f16_bits(w[r]);
             }
         }
     }
-    if (threadIdx.x < C)
-        p.gcum[((int64_t)chunk * Hv + h) * C + threadIdx.x] = G_s[threadIdx.x];
+    if (threadIdx.x < C) {
+        // decay factors the carry multiplies by: gamma_t = exp(G_t) and
+        // exp(G_last - G_t) (G_last = G at the chunk's last token = G_s[C-1])
+        float *gd = p.gcum + ((int64_t)chunk * Hv + h) * 2 * C;
+        gd[threadIdx.x] = __expf(G_s[threadIdx.x]);
+        gd[C + threadIdx.x] = __expf(G_s[C - 1] - G_s[threadIdx.x]);
+    }
 }
 
 // ---------------------------------------------------------------- 3. carry
-
-// One chunk's operands for one wave of the carry, as loaded from the workspace.
-struct CarryOps {
-    half8 w[4], q[4], aq[2], kt[2][2];
-    float u[4], g[4], gl;
-};
-
-__device__ __forceinline__ void load_carry_ops(CarryOps &o, const PrefillParams &p, int chunk,
-                                               int h, int kh, int wave, int li, int lg, int dv0)
-{
-    const int Hv = p.hc.Hv, Hk = p.hc.Hk;
-    const uint16_t *wsrc = p.wmat + ((int64_t)chunk * Hv + h) * C * DH + (wave * 16 + li) * DH + lg * 8;
-    const uint16_t *qsrc = p.qn + ((int64_t)chunk * Hk + kh) * C * DH + (wave * 16 + li) * DH + lg * 8;
-    const uint16_t *asrc = p.aqk + ((int64_t)chunk * Hv + h) * C * C + (wave * 16 + li) * C + lg * 8;
-    const uint16_t *ksrc = p.knT + ((int64_t)chunk * Hk + kh) * DH * C + (wave * 32 + li) * C + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        o.w[ks] = glb_half8(wsrc + ks * 32);
-        o.q[ks] = glb_half8(qsrc + ks * 32);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        o.aq[ks] = glb_half8(asrc + ks * 32);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            o.kt[nt][ks] = glb_half8(ksrc + nt * 16 * C + ks * 32);
-    }
-    const float *usrc = p.umat + ((int64_t)chunk * Hv + h) * C * DH;
-    const float *gsrc = p.gcum + ((int64_t)chunk * Hv + h) * C;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = wave * 16 + lg * 4 + r;
-        o.u[r] = usrc[t * DH + dv0 + li];
-        o.g[r] = gsrc[t];
-    }
-    o.gl = gsrc[C - 1];
-}
 
 // OUT: the output's dtype, or kOutNorm for the f32 buffer the gated norm reads
 constexpr int kOutNorm = 3;
@@ -468,19 +451,122 @@ __device__ __forceinline__ void store_out(const PrefillParams &p, int64_t idx, f
         static_cast<uint16_t *>(p.out)[idx] = f32_to_f16_bits(v);
 }
 
+// LDS image of one chunk's operands for a workgroup covering NU dv slices. Rows are
+// stored with their 16-byte blocks XOR-swizzled so the rows one MFMA operand
+// read touches fall in distinct banks: 256-byte rows (W, Q) use
+// block ^ (row & 15), 128-byte rows (K^T, Aqk) use block ^ ((row >> 1) & 7).
+// u holds the workgroup's 16*NU columns of U, gd the two decay factors per token.
+template <int NU>
+struct ChunkImage {
+    unsigned char w[C * DH * 2];   // W  [t][dk (permuted)]
+    unsigned char q[C * DH * 2];   // Q  [t][dk (permuted)]
+    unsigned char kt[DH * C * 2];  // K^T [dk][t (permuted)]
+    unsigned char aq[C * C * 2];   // Aqk [t][s (permuted)]
+    float u[C][16 * NU];           // U  [t][dv0 .. dv0 + 16 NU), blocks swizzled (NU > 1)
+    float gd[4 * C];               // [t] = gamma_t, [C + t] = exp(G_last - G_t); [2C, 4C) repeats
+};
+
+__device__ __forceinline__ int swz256(int row, int blk) { return row * 256 + 16 * (blk ^ (row & 15)); }
+__device__ __forceinline__ int swz128(int row, int blk) { return row * 128 + 16 * (blk ^ ((row >> 1) & 7)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue the asynchronous global -> LDS copies of one chunk's operands; the
+// NW waves of the workgroup split the 56 one-KiB pieces between them.
+template <int NU>
+__device__ __forceinline__ int swzu(int row, int blk)
+{
+    if constexpr (NU == 1)
+        return blk;  // 64-byte rows: the 16 banks they span are read 4 rows at a time anyway
+    else
+        return blk ^ (2 * ((row >> 2) & 3));
+}
+
+template <int NW, int NU>
+__device__ __forceinline__ void issue_chunk_copy(ChunkImage<NU> &img, const PrefillParams &p, int chunk,
+                                                 int h, int kh, int dvw, int wave, int lane)
+{
+    const int Hv = p.hc.Hv, Hk = p.hc.Hk;
+    const unsigned char *wg = reinterpret_cast<const unsigned char *>(p.wmat + ((int64_t)chunk * Hv + h) * C * DH);
+    const unsigned char *qg = reinterpret_cast<const unsigned char *>(p.qn + ((int64_t)chunk * Hk + kh) * C * DH);
+    const unsigned char *kg = reinterpret_cast<const unsigned char *>(p.knT + ((int64_t)chunk * Hk + kh) * DH * C);
+    const unsigned char *ag = reinterpret_cast<const unsigned char *>(p.aqk + ((int64_t)chunk * Hv + h) * C * C);
+    // W and Q: 16 pieces each of 4 rows x 256 B; K^T: 16 pieces and Aqk: 8
+    // pieces of 8 rows x 128 B. Each lane fetches the global block that the
+    // swizzle places at its 16-byte slot of the piece.
+    static_assert(16 % NW == 0 && 8 % NW == 0, "pieces split evenly");
+#pragma unroll
+    for (int k = 0; k < 16 / NW; ++k) {
+        const int q = k * NW + wave;
+        const int row = 4 * q + (lane >> 4), slot = lane & 15;
+        const int goff = row * 256 + 16 * (slot ^ (row & 15));
+        __builtin_amdgcn_global_load_lds(wg + goff, (lds_void *)(img.w + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qg + goff, (lds_void *)(img.q + q * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 16 / NW; ++k) {
+        const int q = k * NW + wave;
+        const int row = 8 * q + (lane >> 3), slot = lane & 7;
+        __builtin_amdgcn_global_load_lds(kg + row * 128 + 16 * (slot ^ ((row >> 1) & 7)),
+                                         (lds_void *)(img.kt + q * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 8 / NW; ++k) {
+        const int q = k * NW + wave;
+        const int row = 8 * q + (lane >> 3), slot = lane & 7;
+        __builtin_amdgcn_global_load_lds(ag + row * 128 + 16 * (slot ^ ((row >> 1) & 7)),
+                                         (lds_void *)(img.aq + q * 1024), 16, 0, 0);
+    }
+    // U columns [dvw, dvw + 16 NU): rows of 64 NU bytes (4 NU blocks)
+    constexpr int UB = 4 * NU, UROWS = 64 / UB;  // blocks per row, rows per piece
+    static_assert((4 * NU) % NW == 0, "U pieces split evenly");
+    const unsigned char *ug = reinterpret_cast<const unsigned char *>(
+        p.umat + ((int64_t)chunk * Hv + h) * C * DH + dvw);
+#pragma unroll
+    for (int k = 0; k < (4 * NU) / NW; ++k) {
+        const int q = k * NW + wave;
+        const int row = UROWS * q + lane / UB, slot = lane % UB;
+        const int goff = row * (DH * 4) + 16 * swzu<NU>(row, slot);
+        unsigned char *dst = reinterpret_cast<unsigned char *>(&img.u[0][0]) + q * 1024;
+        __builtin_amdgcn_global_load_lds(ug + goff, (lds_void *)dst, 16, 0, 0);
+    }
+    if (wave == 0) {  // 512 bytes of decay factors (lanes 32..63 repeat them)
+        const unsigned char *gg = reinterpret_cast<const unsigned char *>(p.gcum + ((int64_t)chunk * Hv + h) * 2 * C);
+        __builtin_amdgcn_global_load_lds(gg + 16 * (lane & 31), (lds_void *)img.gd, 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ half8 img_read(const unsigned char *base, int off)
+{
+    return *reinterpret_cast<const half8 *>(base + off);
+}
+
+// Carry: one workgroup of 4 waves per (sequence, v-head, 16-row slice of dv),
+// sequential over the sequence's chunks. The state slice S[dv0..dv0+16)[:] lives
+// in MFMA accumulators (f32; wave w holds dk columns 32w..32w+31) with an f16
+// copy in LDS as the B operand of W S^T and Q S^T. Per chunk, wave w owns token
+// rows 16w..16w+15:
+//   P  = W S^T, QS = Q S^T
+//   D  = U - P,  D~ = D exp(G_last - G_t)            (to LDS, token index permuted)
+//   O  = scale (gamma QS + Aqk D)
+//   S <- gamma_last S + D~^T K                       (D~ as an f16 hi + lo pair)
+// The chunk's operands (W, Q, K^T, Aqk, U slice, decay factors) arrive in LDS by
+// asynchronous global->LDS copies issued one chunk ahead into a two-slot ring;
+// outputs are stored one chunk late. Two barriers per chunk.
 template <int OUT>
 __global__ __launch_bounds__(256, 1) void carry_kernel(PrefillParams p)
 {
-    __shared__ __attribute__((aligned(16))) _Float16 Sh[2][DT][KP];  // f16 state slice, ping-pong
-    __shared__ __attribute__((aligned(16))) _Float16 DTl[DT][TP];    // D^T (for Aqk D)
-    __shared__ __attribute__((aligned(16))) _Float16 DsH[DT][TP];    // (decayed D)^T, hi part
-    __shared__ __attribute__((aligned(16))) _Float16 DsL[DT][TP];    // (decayed D)^T, lo part
+    constexpr int NW = 4;
+    __shared__ __attribute__((aligned(16))) ChunkImage<1> img[2];
+    __shared__ __attribute__((aligned(16))) _Float16 Sh[2][DT][KP];   // f16 state slice, dk permuted
+    __shared__ __attribute__((aligned(16))) _Float16 DTl[DT][TP];     // D^T, token permuted
+    __shared__ __attribute__((aligned(16))) _Float16 DsH[DT][TP];     // (decayed D)^T, hi part
+    __shared__ __attribute__((aligned(16))) _Float16 DsL[DT][TP];     // (decayed D)^T, lo part
 
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv;
     constexpr int NT = DH / DT;  // dv slices per head
-    // XCD-aware order: the NT slices of one (sequence, head) share id % 8, so
-    // they run on one XCD and share its L2 for the chunk operands.
+    // XCD-aware order: the NT slices of one (sequence, head) share id % 8
     const int id = blockIdx.x;
     const int group = (id & 7) + 8 * (id / (8 * NT));
     const int slice = (id >> 3) % NT;
@@ -497,7 +583,6 @@ __global__ __launch_bounds__(256, 1) void carry_kernel(PrefillParams p)
     if (nch == 0)
         return;  // empty sequence: state untouched
     const int c0 = p.seq_chunk0[seq];
-    const int clast = c0 + nch - 1;
 
     // state slice: wave w holds dk columns 32w .. 32w+31 as two 16x16 tiles
     float *Sg = p.state + ((int64_t)seq * Hv + h) * DH * DH;
@@ -506,95 +591,99 @@ __global__ __launch_bounds__(256, 1) void carry_kernel(PrefillParams p)
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int dv = dv0 + lg * 4 + r, dk = wave * 32 + nt * 16 + li;
-            S[nt][r] = Sg[(int64_t)dv * DH + dk];
-            Sh[0][lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
+            const int dk = wave * 32 + nt * 16 + li;
+            S[nt][r] = Sg[(int64_t)(dv0 + lg * 4 + r) * DH + dk];
+            Sh[0][lg * 4 + r][perm_pos(dk)] = (_Float16)S[nt][r];
         }
-    __syncthreads();
 
-    // One chunk with operands `o`, reading the state copy Sh[ci & 1] and leaving
-    // the new one in Sh[(ci + 1) & 1]: two barriers per chunk.
-    auto process = [&](const CarryOps &o, int ci) {
-        const int tok0 = start + ci * C;
-        const int n = min(C, len - ci * C);
+    issue_chunk_copy<NW, 1>(img[0], p, c0, h, kh, dv0, wave, lane);
+    f32x4 Oprev = {0.f, 0.f, 0.f, 0.f};
+    int prev_tok0 = 0, prev_n = 0;
+
+    for (int ci = 0; ci < nch; ++ci) {
+        // this chunk's copies (issued one iteration ago), older stores, LDS writes
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (ci > 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = wave * 16 + lg * 4 + r;
+                if (t < prev_n)
+                    store_out<OUT>(p, ((int64_t)(prev_tok0 + t) * Hv + h) * DH + dv0 + li,
+                                   hc.scale * Oprev[r]);
+            }
+        }
+        if (ci + 1 < nch)
+            issue_chunk_copy<NW, 1>(img[(ci + 1) & 1], p, c0 + ci + 1, h, kh, dv0, wave, lane);
+        const ChunkImage<1> &cur = img[ci & 1];
         const int sb = ci & 1;
-        // P = W S0^T and QS = Q S0^T for token rows 16w..16w+15 (B operand: S0 rows)
+
+        // P = W S0^T and QS = Q S0^T for token rows 16w..16w+15
         f32x4 P = {0.f, 0.f, 0.f, 0.f}, QS = {0.f, 0.f, 0.f, 0.f};
+        const int trow = wave * 16 + li;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const half8 b = lds_half8(&Sh[sb][li][ks * 32 + lg * 8]);
-            P = mfma16(o.w[ks], b, P);
-            QS = mfma16(o.q[ks], b, QS);
+            P = mfma16(img_read(cur.w, swz256(trow, 4 * ks + lg)), b, P);
+            QS = mfma16(img_read(cur.q, swz256(trow, 4 * ks + lg)), b, QS);
         }
-        // D = U - P; decayed D for the state update, as an f16 hi + lo pair
+        // D = U - P; the decayed D as an f16 hi + lo pair; gamma QS
         f32x4 O;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = wave * 16 + lg * 4 + r;
-            const float d = o.u[r] - P[r];
-            const float ds = d * __expf(o.gl - o.g[r]);
+            const float d = cur.u[t][li] - P[r];
+            const float ds = d * cur.gd[C + t];
             const _Float16 dh = (_Float16)ds;
-            DTl[li][t] = (_Float16)d;
-            DsH[li][t] = dh;
-            DsL[li][t] = (_Float16)(ds - (float)dh);
-            O[r] = __expf(o.g[r]) * QS[r];
+            const int tp = perm_pos(t);
+            DTl[li][tp] = (_Float16)d;
+            DsH[li][tp] = dh;
+            DsL[li][tp] = (_Float16)(ds - (float)dh);
+            O[r] = cur.gd[t] * QS[r];
         }
-        __syncthreads();
-        // O = scale (gamma QS + Aqk D)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+
+        // O += Aqk D (only the token blocks at or below this wave's rows)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            O = mfma16(o.aq[ks], lds_half8(&DTl[li][ks * 32 + lg * 8]), O);
-        // S_n = gamma_{n-1} S0 + D~^T K, D~ = hi + lo
-        const float gn = __expf(o.gl);
+            if (2 * ks <= wave)
+                O = mfma16(img_read(cur.aq, swz128(trow, 4 * ks + lg)),
+                           lds_half8(&DTl[li][ks * 32 + lg * 8]), O);
+        // S_n = gamma_last S0 + D~^T K
+        const float gn = cur.gd[C - 1];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             S[nt] *= gn;
+            const int krow = wave * 32 + nt * 16 + li;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                S[nt] = mfma16(lds_half8(&DsH[li][ks * 32 + lg * 8]), o.kt[nt][ks], S[nt]);
-                S[nt] = mfma16(lds_half8(&DsL[li][ks * 32 + lg * 8]), o.kt[nt][ks], S[nt]);
+                const half8 kb = img_read(cur.kt, swz128(krow, 4 * ks + lg));
+                S[nt] = mfma16(lds_half8(&DsH[li][ks * 32 + lg * 8]), kb, S[nt]);
+                S[nt] = mfma16(lds_half8(&DsL[li][ks * 32 + lg * 8]), kb, S[nt]);
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = wave * 16 + lg * 4 + r;
-            if (t < n)
-                store_out<OUT>(p, ((int64_t)(tok0 + t) * Hv + h) * DH + dv0 + li, hc.scale * O[r]);
-        }
+        Oprev = O;
+        prev_tok0 = start + ci * C;
+        prev_n = min(C, len - ci * C);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Sh[sb ^ 1][lg * 4 + r][wave * 32 + nt * 16 + li] = (_Float16)S[nt][r];
-        __syncthreads();  // the new state copy is complete; D may be overwritten
-    };
-
-    // Operands are prefetched two chunks ahead through three register buffers
-    // (indices past the sequence's last chunk re-load the last one, harmlessly).
-    CarryOps A, B, Cb;
-    load_carry_ops(A, p, c0, h, kh, wave, li, lg, dv0);
-    load_carry_ops(B, p, min(c0 + 1, clast), h, kh, wave, li, lg, dv0);
-    for (int ci = 0;;) {
-        load_carry_ops(Cb, p, min(c0 + ci + 2, clast), h, kh, wave, li, lg, dv0);
-        process(A, ci);
-        if (++ci == nch)
-            break;
-        load_carry_ops(A, p, min(c0 + ci + 2, clast), h, kh, wave, li, lg, dv0);
-        process(B, ci);
-        if (++ci == nch)
-            break;
-        load_carry_ops(B, p, min(c0 + ci + 2, clast), h, kh, wave, li, lg, dv0);
-        process(Cb, ci);
-        if (++ci == nch)
-            break;
+                Sh[sb ^ 1][lg * 4 + r][perm_pos(wave * 32 + nt * 16 + li)] = (_Float16)S[nt][r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = wave * 16 + lg * 4 + r;
+        if (t < prev_n)
+            store_out<OUT>(p, ((int64_t)(prev_tok0 + t) * Hv + h) * DH + dv0 + li,
+                           hc.scale * Oprev[r]);
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int dv = dv0 + lg * 4 + r, dk = wave * 32 + nt * 16 + li;
-            Sg[(int64_t)dv * DH + dk] = S[nt][r];
-        }
+        for (int r = 0; r < 4; ++r)
+            Sg[(int64_t)(dv0 + lg * 4 + r) * DH + wave * 32 + nt * 16 + li] = S[nt][r];
 }
 
 // ---------------------------------------------------------------- 4. gated norm
