@@ -22,6 +22,9 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # keep MFMA accumulators in ordinary VGPRs: the prefill carry scales
+           # and converts its accumulators with VALU work every chunk
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wall", "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            ] + [f"-D{d}" for d in defines] + ["-x", "hip"] + srcs + ["-o", out + ".tmp"]

@@ -72,9 +72,9 @@ struct PrefillParams {
     uint16_t *qn;          // [num_chunks][Hk][64][dk]   f16, normalised q rows
     uint16_t *knT;         // [num_chunks][Hk][dk][64]   f16, normalised k, transposed
     uint16_t *wmat;        // [num_chunks][Hv][64][dk]   f16, W = T diag(beta*gamma) K
-    float *umat;           // [num_chunks][Hv][64][dv]   f32, U = T diag(beta) V
-    uint16_t *aqk;         // [num_chunks][Hv][64][64]   f16, masked decayed Q K^T
-    float *gcum;           // [num_chunks][Hv][64]       f32, in-chunk prefix sums G_t of g
+    float *umat;           // [num_chunks][Hv][dv][64]   f32, -U^T with U = T diag(beta) V
+    uint16_t *aqk;         // [num_chunks][Hv][64][64]   f16, -scale (masked decayed Q K^T)
+    float *gcum;           // [num_chunks][Hv][4][64]    f32, exp(G_t), -exp(G_last - G_t), scale exp(G_t), 0
     float *onorm;          // [total][Hv][dv]            f32 core output (gated norm only)
 };
 

@@ -49,7 +49,6 @@ constexpr int DH = 128;       // head dim (dk = dv) of the built prefill
 constexpr int KP = DH + 8;    // padded f16 row (272 B): conflict-free 16-B MFMA operand reads
 constexpr int TP = C + 8;     // padded f16 row of a transposed [dim][token] tile (144 B)
 constexpr int AP = C + 4;     // padded f32 row of the 64x64 A / T matrix
-constexpr int DT = 16;        // dv rows per carry workgroup
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
 {
@@ -108,7 +107,7 @@ WsLayout ws_layout(int Hk, int Hv, int64_t MC, int N, int64_t total_tokens, bool
     L.wmat = take(sizeof(uint16_t) * MC * Hv * C * DH);
     L.umat = take(sizeof(float) * MC * Hv * C * DH);
     L.aqk = take(sizeof(uint16_t) * MC * Hv * C * C);
-    L.gcum = take(sizeof(float) * MC * Hv * 2 * C);
+    L.gcum = take(sizeof(float) * MC * Hv * 4 * C);
     L.onorm = norm ? take(sizeof(float) * (size_t)total_tokens * Hv * DH) : off;
     L.total = off;
     return L;
@@ -172,6 +171,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 
     _Float16(*Kh)[KP] = reinterpret_cast<_Float16(*)[KP]>(X1);
     _Float16(*Qh)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);
+    // f16 remainders (x - f16(x)) of the normalised rows, for Q K^T; they live
+    // in the transposed tiles' space, which is filled only after that product
+    _Float16(*Kl)[KP] = reinterpret_cast<_Float16(*)[KP]>(&VbT[0][0]);
+    _Float16(*Ql)[KP] = reinterpret_cast<_Float16(*)[KP]>(&KbT[0][0]);
+    static_assert(sizeof(VbT) >= C * KP * 2, "VbT holds the K remainders");
     float(*Am)[AP] = reinterpret_cast<float(*)[AP]>(X1);
     float(*Pm)[36] = reinterpret_cast<float(*)[36]>(X2);
 
@@ -239,41 +243,36 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             }
             const float keep = t < n ? 1.f : 0.f;
             typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-            const half4 kh4 = {(_Float16)(keep * kk.x), (_Float16)(keep * kk.y),
-                               (_Float16)(keep * kk.z), (_Float16)(keep * kk.w)};
-            const half4 qh4 = {(_Float16)(keep * qq.x), (_Float16)(keep * qq.y),
-                               (_Float16)(keep * qq.z), (_Float16)(keep * qq.w)};
+            const float4 kz = make_float4(keep * kk.x, keep * kk.y, keep * kk.z, keep * kk.w);
+            const float4 qz = make_float4(keep * qq.x, keep * qq.y, keep * qq.z, keep * qq.w);
+            const half4 kh4 = {(_Float16)kz.x, (_Float16)kz.y, (_Float16)kz.z, (_Float16)kz.w};
+            const half4 qh4 = {(_Float16)qz.x, (_Float16)qz.y, (_Float16)qz.z, (_Float16)qz.w};
+            const half4 kl4 = {(_Float16)(kz.x - (float)kh4[0]), (_Float16)(kz.y - (float)kh4[1]),
+                               (_Float16)(kz.z - (float)kh4[2]), (_Float16)(kz.w - (float)kh4[3])};
+            const half4 ql4 = {(_Float16)(qz.x - (float)qh4[0]), (_Float16)(qz.y - (float)qh4[1]),
+                               (_Float16)(qz.z - (float)qh4[2]), (_Float16)(qz.w - (float)qh4[3])};
             *reinterpret_cast<half4 *>(&Kh[t][c4]) = kh4;
             *reinterpret_cast<half4 *>(&Qh[t][c4]) = qh4;
+            *reinterpret_cast<half4 *>(&Kl[t][c4]) = kl4;
+            *reinterpret_cast<half4 *>(&Ql[t][c4]) = ql4;
         }
     }
     __syncthreads();
 
-    // -- transposed tiles, one (dim, 8-token octet) item per 16-byte LDS write:
-    // beta v from the input (lanes along dim: coalesced), beta gamma k from the
-    // f16 rows just written (the same rounded K the gram and the carry use).
+    // the v elements of the transposed tiles built after the products below:
+    // their loads are issued now so that the products hide their latency
+    constexpr int kTileIters = (DH * C / 8) / 256;
+    uint32_t vr[kTileIters][8];
 #pragma unroll
-    for (int it = 0; it < (DH * C / 8) / 256; ++it) {
+    for (int it = 0; it < kTileIters; ++it) {
         const int e = it * 256 + threadIdx.x;
         const int j = e % DH, o = e / DH;
-        half8 vb, kb;
-        uint32_t vr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t r = tok0 + min(o * 8 + i, n - 1);
-            vr[i] = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DH + j);
+            vr[it][i] = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DH + j);
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = o * 8 + i;
-            const float bt = beta_s[t];  // 0 for tokens past the chunk's end
-            vb[i] = (_Float16)(bt * raw1_to_f32<QT>(vr[i]));
-            kb[i] = (_Float16)(bt * __expf(G_s[t]) * (float)Kh[t][j]);
-        }
-        *reinterpret_cast<half8 *>(&VbT[j][o * 8]) = vb;
-        *reinterpret_cast<half8 *>(&KbT[j][o * 8]) = kb;
     }
-    __syncthreads();
 
     // -- K K^T and Q K^T on the lower block triangle: wave w owns token rows 16w..
     const int li = lane & 15, lg = lane >> 4;
@@ -287,11 +286,37 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             for (int ks = 0; ks < 4; ++ks) {
                 const half8 ka = lds_half8(&Kh[wave * 16 + li][ks * 32 + lg * 8]);
                 const half8 qa = lds_half8(&Qh[wave * 16 + li][ks * 32 + lg * 8]);
+                const half8 ql = lds_half8(&Ql[wave * 16 + li][ks * 32 + lg * 8]);
                 const half8 kb = lds_half8(&Kh[j * 16 + li][ks * 32 + lg * 8]);
+                const half8 kl = lds_half8(&Kl[j * 16 + li][ks * 32 + lg * 8]);
                 gram[j] = mfma16(ka, kb, gram[j]);
+                // Q K^T from hi + lo parts of both (the lo x lo term is below f32 rounding)
                 qk[j] = mfma16(qa, kb, qk[j]);
+                qk[j] = mfma16(qa, kl, qk[j]);
+                qk[j] = mfma16(ql, kb, qk[j]);
             }
         }
+    }
+
+    __syncthreads();  // the remainders are dead: the transposed tiles take their space
+
+    // -- transposed tiles, one (dim, 8-token octet) item per 16-byte LDS write:
+    // beta v from the input (lanes along dim: coalesced), beta gamma k from the
+    // f16 rows just written (the same rounded K the gram and the carry use).
+#pragma unroll
+    for (int it = 0; it < kTileIters; ++it) {
+        const int e = it * 256 + threadIdx.x;
+        const int j = e % DH, o = e / DH;
+        half8 vb, kb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = o * 8 + i;
+            const float bt = beta_s[t];  // 0 for tokens past the chunk's end
+            vb[i] = (_Float16)(bt * raw1_to_f32<QT>(vr[it][i]));
+            kb[i] = (_Float16)(bt * __expf(G_s[t]) * (float)Kh[t][j]);
+        }
+        *reinterpret_cast<half8 *>(&VbT[j][o * 8]) = vb;
+        *reinterpret_cast<half8 *>(&KbT[j][o * 8]) = kb;
     }
 
     // normalised Q rows and K^T go to the workspace for the carry
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
                 const int t = wave * 16 + lg * 4 + r, s = j * 16 + li;
                 const float dg = s <= t ? __expf(G_s[t] - G_s[s]) : 0.f;
                 Am[t][s] = s < t ? beta_s[t] * dg * gram[j][r] : 0.f;
-                aq[t * C + perm_pos(s)] = f32_to_f16_bits(dg * qk[j][r]);
+                aq[t * C + perm_pos(s)] = f32_to_f16_bits(-hc.scale * dg * qk[j][r]);
             }
         }
     }
@@ -406,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 ta[ks][i] = (_Float16)Am[wave * 16 + li][ks * 32 + lg * 8 + i];
-        float *ud = p.umat + ((int64_t)chunk * Hv + h) * C * DH;
+        float *ud = p.umat + ((int64_t)chunk * Hv + h) * DH * C;
         uint16_t *wd = p.wmat + ((int64_t)chunk * Hv + h) * C * DH;
 #pragma unroll
         for (int nt = 0; nt < DH / 16; ++nt) {
@@ -416,20 +441,25 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
                 u = mfma16(ta[ks], lds_half8(&VbT[nt * 16 + li][ks * 32 + lg * 8]), u);
                 w = mfma16(ta[ks], lds_half8(&KbT[nt * 16 + li][ks * 32 + lg * 8]), w);
             }
+            // -U^T: this lane's four tokens are adjacent in row dv
+            *reinterpret_cast<f32x4 *>(ud + (nt * 16 + li) * C + wave * 16 + lg * 4) = -u;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = wave * 16 + lg * 4 + r;
-                ud[t * DH + nt * 16 + li] = u[r];
                 wd[t * DH + perm_pos(nt * 16 + li)] = f32_to_f16_bits(w[r]);
             }
         }
     }
     if (threadIdx.x < C) {
-        // decay factors the carry multiplies by: gamma_t = exp(G_t) and
-        // exp(G_last - G_t) (G_last = G at the chunk's last token = G_s[C-1])
-        float *gd = p.gcum + ((int64_t)chunk * Hv + h) * 2 * C;
-        gd[threadIdx.x] = __expf(G_s[threadIdx.x]);
-        gd[C + threadIdx.x] = __expf(G_s[C - 1] - G_s[threadIdx.x]);
+        // decay rows the carry multiplies by: gamma_t = exp(G_t),
+        // -exp(G_last - G_t) (negated because the carry holds -D) and
+        // scale gamma_t; G_last = G at the chunk's last token = G_s[C-1]
+        float *gd = p.gcum + ((int64_t)chunk * Hv + h) * 4 * C;
+        const float gm = __expf(G_s[threadIdx.x]);
+        gd[threadIdx.x] = gm;
+        gd[C + threadIdx.x] = -__expf(G_s[C - 1] - G_s[threadIdx.x]);
+        gd[2 * C + threadIdx.x] = hc.scale * gm;
+        gd[3 * C + threadIdx.x] = 0.f;
     }
 }
 
@@ -438,145 +468,203 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 // OUT: the output's dtype, or kOutNorm for the f32 buffer the gated norm reads
 constexpr int kOutNorm = 3;
 
-template <int OUT>
-__device__ __forceinline__ void store_out(const PrefillParams &p, int64_t idx, float v)
-{
-    if constexpr (OUT == kOutNorm)
-        p.onorm[idx] = v;
-    else if constexpr (OUT == DT_F32)
-        static_cast<float *>(p.out)[idx] = v;
-    else if constexpr (OUT == DT_BF16)
-        static_cast<uint16_t *>(p.out)[idx] = f32_to_bf16_bits(v);
-    else
-        static_cast<uint16_t *>(p.out)[idx] = f32_to_f16_bits(v);
-}
-
-// LDS image of one chunk's operands for a workgroup covering NU dv slices. Rows are
-// stored with their 16-byte blocks XOR-swizzled so the rows one MFMA operand
-// read touches fall in distinct banks: 256-byte rows (W, Q) use
-// block ^ (row & 15), 128-byte rows (K^T, Aqk) use block ^ ((row >> 1) & 7).
-// u holds the workgroup's 16*NU columns of U, gd the two decay factors per token.
+// LDS image of one chunk's operands for a workgroup covering NU 16-row dv
+// slices. Rows are stored with their 16-byte blocks XOR-swizzled so that the 16
+// rows one MFMA operand read touches fall in distinct banks: 256-byte rows (W, Q,
+// -U^T) use block ^ (row & 15), 128-byte rows (K^T, Aqk) block ^ ((row >> 1) & 7).
 template <int NU>
 struct ChunkImage {
-    unsigned char w[C * DH * 2];   // W  [t][dk (permuted)]
-    unsigned char q[C * DH * 2];   // Q  [t][dk (permuted)]
-    unsigned char kt[DH * C * 2];  // K^T [dk][t (permuted)]
-    unsigned char aq[C * C * 2];   // Aqk [t][s (permuted)]
-    float u[C][16 * NU];           // U  [t][dv0 .. dv0 + 16 NU), blocks swizzled (NU > 1)
-    float gd[4 * C];               // [t] = gamma_t, [C + t] = exp(G_last - G_t); [2C, 4C) repeats
+    unsigned char w[C * DH * 2];      // W   [t][dk (permuted)]        f16
+    unsigned char q[C * DH * 2];      // Q   [t][dk (permuted)]        f16
+    unsigned char kt[DH * C * 2];     // K^T [dk][t (permuted)]        f16
+    unsigned char aq[C * C * 2];      // -scale Aqk [t][s (permuted)]  f16
+    unsigned char u[16 * NU * C * 4]; // -U^T [dv - dvw][t]            f32
+    float gd[4 * C];                  // decay rows, as the prep writes them
 };
-
-__device__ __forceinline__ int swz256(int row, int blk) { return row * 256 + 16 * (blk ^ (row & 15)); }
-__device__ __forceinline__ int swz128(int row, int blk) { return row * 128 + 16 * (blk ^ ((row >> 1) & 7)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issue the asynchronous global -> LDS copies of one chunk's operands; the
-// NW waves of the workgroup split the 56 one-KiB pieces between them.
-template <int NU>
-__device__ __forceinline__ int swzu(int row, int blk)
+// One asynchronous 16-byte-per-lane global -> LDS copy: lane l's bytes land at
+// dst + 16 l (dst must be wave-uniform).
+__device__ __forceinline__ void dma16(const unsigned char *src, unsigned char *dst)
 {
-    if constexpr (NU == 1)
-        return blk;  // 64-byte rows: the 16 banks they span are read 4 rows at a time anyway
-    else
-        return blk ^ (2 * ((row >> 2) & 3));
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
 }
 
+// Per-lane byte offsets of the global blocks a lane copies; they depend on the
+// lane and the piece only, not on the chunk.
 template <int NW, int NU>
-__device__ __forceinline__ void issue_chunk_copy(ChunkImage<NU> &img, const PrefillParams &p, int chunk,
-                                                 int h, int kh, int dvw, int wave, int lane)
+struct CopyOffsets {
+    uint32_t row256[16 / NW], row128[16 / NW], aq[8 / NW], u[(4 * NU) / NW];
+};
+
+template <int NW, int NU>
+__device__ __forceinline__ CopyOffsets<NW, NU> copy_offsets(int wave, int lane)
+{
+    CopyOffsets<NW, NU> o;
+    const int r256 = lane >> 4, s256 = lane & 15, r128 = lane >> 3, s128 = lane & 7;
+#pragma unroll
+    for (int k = 0; k < 16 / NW; ++k) {
+        const int q = k * NW + wave;
+        const int row = 4 * q + r256, krow = 8 * q + r128;
+        o.row256[k] = row * 256 + 16 * (s256 ^ (row & 15));
+        o.row128[k] = krow * 128 + 16 * (s128 ^ ((krow >> 1) & 7));
+    }
+#pragma unroll
+    for (int k = 0; k < 8 / NW; ++k) {
+        const int row = 8 * (k * NW + wave) + r128;
+        o.aq[k] = row * 128 + 16 * (s128 ^ ((row >> 1) & 7));
+    }
+#pragma unroll
+    for (int k = 0; k < (4 * NU) / NW; ++k) {
+        const int row = 4 * (k * NW + wave) + r256;
+        o.u[k] = row * 256 + 16 * (s256 ^ (row & 15));
+    }
+    return o;
+}
+
+// Issue the asynchronous global -> LDS copies of one chunk's operands; the NW
+// waves of the workgroup split the one-KiB pieces between them (wave must be
+// wave-uniform: it selects the LDS destination).
+template <int NW, int NU>
+__device__ __forceinline__ void issue_chunk_copy(ChunkImage<NU> &img, const PrefillParams &p,
+                                                 const CopyOffsets<NW, NU> &o, int chunk, int h, int kh,
+                                                 int dvw, int wave, int lane)
 {
     const int Hv = p.hc.Hv, Hk = p.hc.Hk;
     const unsigned char *wg = reinterpret_cast<const unsigned char *>(p.wmat + ((int64_t)chunk * Hv + h) * C * DH);
     const unsigned char *qg = reinterpret_cast<const unsigned char *>(p.qn + ((int64_t)chunk * Hk + kh) * C * DH);
     const unsigned char *kg = reinterpret_cast<const unsigned char *>(p.knT + ((int64_t)chunk * Hk + kh) * DH * C);
     const unsigned char *ag = reinterpret_cast<const unsigned char *>(p.aqk + ((int64_t)chunk * Hv + h) * C * C);
-    // W and Q: 16 pieces each of 4 rows x 256 B; K^T: 16 pieces and Aqk: 8
-    // pieces of 8 rows x 128 B. Each lane fetches the global block that the
-    // swizzle places at its 16-byte slot of the piece.
-    static_assert(16 % NW == 0 && 8 % NW == 0, "pieces split evenly");
+    const unsigned char *ug = reinterpret_cast<const unsigned char *>(p.umat + (((int64_t)chunk * Hv + h) * DH + dvw) * C);
+    static_assert(16 % NW == 0 && 8 % NW == 0 && (4 * NU) % NW == 0, "pieces split evenly");
 #pragma unroll
     for (int k = 0; k < 16 / NW; ++k) {
         const int q = k * NW + wave;
-        const int row = 4 * q + (lane >> 4), slot = lane & 15;
-        const int goff = row * 256 + 16 * (slot ^ (row & 15));
-        __builtin_amdgcn_global_load_lds(wg + goff, (lds_void *)(img.w + q * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(qg + goff, (lds_void *)(img.q + q * 1024), 16, 0, 0);
+        dma16(wg + o.row256[k], img.w + q * 1024);
+        dma16(qg + o.row256[k], img.q + q * 1024);
+        dma16(kg + o.row128[k], img.kt + q * 1024);
     }
 #pragma unroll
-    for (int k = 0; k < 16 / NW; ++k) {
-        const int q = k * NW + wave;
-        const int row = 8 * q + (lane >> 3), slot = lane & 7;
-        __builtin_amdgcn_global_load_lds(kg + row * 128 + 16 * (slot ^ ((row >> 1) & 7)),
-                                         (lds_void *)(img.kt + q * 1024), 16, 0, 0);
-    }
+    for (int k = 0; k < 8 / NW; ++k)
+        dma16(ag + o.aq[k], img.aq + (k * NW + wave) * 1024);
 #pragma unroll
-    for (int k = 0; k < 8 / NW; ++k) {
-        const int q = k * NW + wave;
-        const int row = 8 * q + (lane >> 3), slot = lane & 7;
-        __builtin_amdgcn_global_load_lds(ag + row * 128 + 16 * (slot ^ ((row >> 1) & 7)),
-                                         (lds_void *)(img.aq + q * 1024), 16, 0, 0);
-    }
-    // U columns [dvw, dvw + 16 NU): rows of 64 NU bytes (4 NU blocks)
-    constexpr int UB = 4 * NU, UROWS = 64 / UB;  // blocks per row, rows per piece
-    static_assert((4 * NU) % NW == 0, "U pieces split evenly");
-    const unsigned char *ug = reinterpret_cast<const unsigned char *>(
-        p.umat + ((int64_t)chunk * Hv + h) * C * DH + dvw);
-#pragma unroll
-    for (int k = 0; k < (4 * NU) / NW; ++k) {
-        const int q = k * NW + wave;
-        const int row = UROWS * q + lane / UB, slot = lane % UB;
-        const int goff = row * (DH * 4) + 16 * swzu<NU>(row, slot);
-        unsigned char *dst = reinterpret_cast<unsigned char *>(&img.u[0][0]) + q * 1024;
-        __builtin_amdgcn_global_load_lds(ug + goff, (lds_void *)dst, 16, 0, 0);
-    }
-    if (wave == 0) {  // 512 bytes of decay factors (lanes 32..63 repeat them)
-        const unsigned char *gg = reinterpret_cast<const unsigned char *>(p.gcum + ((int64_t)chunk * Hv + h) * 2 * C);
-        __builtin_amdgcn_global_load_lds(gg + 16 * (lane & 31), (lds_void *)img.gd, 16, 0, 0);
+    for (int k = 0; k < (4 * NU) / NW; ++k)
+        dma16(ug + o.u[k], img.u + (k * NW + wave) * 1024);
+    if (wave == 0) {  // the 1 KiB of decay rows
+        const unsigned char *gg = reinterpret_cast<const unsigned char *>(p.gcum + ((int64_t)chunk * Hv + h) * 4 * C);
+        dma16(gg + 16 * lane, reinterpret_cast<unsigned char *>(img.gd));
     }
 }
 
-__device__ __forceinline__ half8 img_read(const unsigned char *base, int off)
+__device__ __forceinline__ half8 img_half8(const unsigned char *base, int off)
 {
     return *reinterpret_cast<const half8 *>(base + off);
 }
-
-// Carry: one workgroup of 4 waves per (sequence, v-head, 16-row slice of dv),
-// sequential over the sequence's chunks. The state slice S[dv0..dv0+16)[:] lives
-// in MFMA accumulators (f32; wave w holds dk columns 32w..32w+31) with an f16
-// copy in LDS as the B operand of W S^T and Q S^T. Per chunk, wave w owns token
-// rows 16w..16w+15:
-//   P  = W S^T, QS = Q S^T
-//   D  = U - P,  D~ = D exp(G_last - G_t)            (to LDS, token index permuted)
-//   O  = scale (gamma QS + Aqk D)
-//   S <- gamma_last S + D~^T K                       (D~ as an f16 hi + lo pair)
-// The chunk's operands (W, Q, K^T, Aqk, U slice, decay factors) arrive in LDS by
-// asynchronous global->LDS copies issued one chunk ahead into a two-slot ring;
-// outputs are stored one chunk late. Two barriers per chunk.
-template <int OUT>
-__global__ __launch_bounds__(256, 1) void carry_kernel(PrefillParams p)
+__device__ __forceinline__ f32x4 img_f32x4(const unsigned char *base, int off)
 {
-    constexpr int NW = 4;
-    __shared__ __attribute__((aligned(16))) ChunkImage<1> img[2];
-    __shared__ __attribute__((aligned(16))) _Float16 Sh[2][DT][KP];   // f16 state slice, dk permuted
-    __shared__ __attribute__((aligned(16))) _Float16 DTl[DT][TP];     // D^T, token permuted
-    __shared__ __attribute__((aligned(16))) _Float16 DsH[DT][TP];     // (decayed D)^T, hi part
-    __shared__ __attribute__((aligned(16))) _Float16 DsL[DT][TP];     // (decayed D)^T, lo part
+    return *reinterpret_cast<const f32x4 *>(base + off);
+}
+
+// Two 16x16 accumulator tiles (rows r and r + 16 of a 32-block) as the eight
+// f16 k-values one lane supplies to a 16x16x32 product, in the permuted order.
+__device__ __forceinline__ half8 pack_tiles(const f32x4 &lo, const f32x4 &hi)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = __builtin_convertvector((f2){lo[0], lo[1]}, h2);
+    const h2 b = __builtin_convertvector((f2){lo[2], lo[3]}, h2);
+    const h2 c = __builtin_convertvector((f2){hi[0], hi[1]}, h2);
+    const h2 d = __builtin_convertvector((f2){hi[2], hi[3]}, h2);
+    return (half8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int V>
+struct Slot {
+    static constexpr int value = V;
+};
+
+// One output element through a buffer resource (offset in bytes).
+template <int OUT>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, uint32_t off, float x)
+{
+    if constexpr (OUT == DT_F32 || OUT == kOutNorm) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
+    } else {
+        // round to nearest even in hardware (v_cvt_pk_{bf16,f16}_f32)
+        uint16_t v;
+        if constexpr (OUT == DT_BF16) {
+            const __bf16 b = (__bf16)x;
+            __builtin_memcpy(&v, &b, 2);
+        } else {
+            v = f32_to_f16_bits(x);
+        }
+        __builtin_amdgcn_raw_buffer_store_b16(v, rs, off, 0, 0);
+    }
+}
+
+// Output rows of one chunk (n valid tokens from token tok0). A full chunk
+// stores without branches; a partial one masks the padding rows. The buffer
+// resource's extent ends at the chunk's last valid row either way.
+template <int OUT>
+__device__ __forceinline__ void store_rows(const PrefillParams &p, int tok0, int n, int h, int64_t orow,
+                                           uint32_t lane_off, int lg, const f32x4 (&O)[4])
+{
+    constexpr int ES = OUT == DT_F32 || OUT == kOutNorm ? 4 : 2;
+    void *base = OUT == kOutNorm ? static_cast<void *>(p.onorm) : p.out;
+    unsigned char *b = static_cast<unsigned char *>(base) + ((int64_t)tok0 * orow + (int64_t)h * DH) * ES;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)(n * orow * ES), 0x00020000);
+    const uint32_t rstride = (uint32_t)(orow * ES);  // bytes per token row
+    if (n == C) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                store_elem<OUT>(rs, lane_off + (16 * j + r) * rstride, O[j][r]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * j + 4 * lg + r < n)
+                    store_elem<OUT>(rs, lane_off + (16 * j + r) * rstride, O[j][r]);
+    }
+}
+
+// Carry: sequential over a sequence's chunks, one wave per 16-row slice of dv,
+// NW slices (of one v-head) per workgroup. Wave state: S^T[dk][dv] for its 16
+// dv columns in eight 16x16 f32 accumulator tiles, which also serve directly
+// (rounded to f16) as the B operand of W S^T and Q S^T, so the chain from one
+// chunk's state to the next never leaves the wave:
+//   P' = W S^T - U  (= -D)                      accumulator seeded with -U
+//   O  = scale gamma Q S^T + (-scale Aqk)(-D)      -D as an f16 hi + lo pair
+//   S^T <- gamma_last S^T + K^T (D e)           D e as an f16 hi + lo pair
+// with e_t = exp(G_last - G_t). The chunk's operands arrive in LDS through
+// asynchronous global->LDS copies issued one chunk ahead into a two-slot ring
+// shared by the workgroup's waves; outputs are stored one chunk late. One
+// barrier per chunk.
+template <int NW, int OUT>
+__global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
+{
+    __shared__ __attribute__((aligned(16))) ChunkImage<NW> img[2];
 
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv;
-    constexpr int NT = DH / DT;  // dv slices per head
-    // XCD-aware order: the NT slices of one (sequence, head) share id % 8
+    constexpr int NG = DH / (16 * NW);  // workgroups per (sequence, v-head)
+    // XCD-aware order: the NG workgroups of one (sequence, head) share id % 8
     const int id = blockIdx.x;
-    const int group = (id & 7) + 8 * (id / (8 * NT));
-    const int slice = (id >> 3) % NT;
+    const int group = (id & 7) + 8 * (id / (8 * NG));
+    const int part = (id >> 3) % NG;
     if (group >= p.N * Hv)
         return;
     const int seq = group / Hv, h = group % Hv;
     const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
-    const int dv0 = slice * DT;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int dvw = part * 16 * NW;  // the workgroup's first dv row
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
+    const int dvl = dvw + wave * 16 + li;  // this lane's dv row
     const int start = p.cu[seq];
     const int len = p.cu[seq + 1] - start;
     const int nch = (len + C - 1) / C;
@@ -584,106 +672,152 @@ __global__ __launch_bounds__(256, 1) void carry_kernel(PrefillParams p)
         return;  // empty sequence: state untouched
     const int c0 = p.seq_chunk0[seq];
 
-    // state slice: wave w holds dk columns 32w .. 32w+31 as two 16x16 tiles
-    float *Sg = p.state + ((int64_t)seq * Hv + h) * DH * DH;
-    f32x4 S[2];
+    // ST[m][r] = S[dvl][16m + 4lg + r]
+    float *Sg = p.state + (((int64_t)seq * Hv + h) * DH + dvl) * DH + 4 * lg;
+    f32x4 ST[8];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int dk = wave * 32 + nt * 16 + li;
-            S[nt][r] = Sg[(int64_t)(dv0 + lg * 4 + r) * DH + dk];
-            Sh[0][lg * 4 + r][perm_pos(dk)] = (_Float16)S[nt][r];
-        }
+    for (int m = 0; m < 8; ++m)
+        ST[m] = *reinterpret_cast<const f32x4 *>(Sg + 16 * m);
 
-    issue_chunk_copy<NW, 1>(img[0], p, c0, h, kh, dv0, wave, lane);
-    f32x4 Oprev = {0.f, 0.f, 0.f, 0.f};
+    const CopyOffsets<NW, NW> co = copy_offsets<NW, NW>(wave, lane);
+    issue_chunk_copy<NW, NW>(img[0], p, co, c0, h, kh, dvw, wave, lane);
+
+    // per-lane byte offsets of the swizzled operand reads
+    int wq[4], ka[2], uo[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        wq[ks] = li * 256 + 16 * ((4 * ks + lg) ^ li);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+        ka[ks] = li * 128 + 16 * ((4 * ks + lg) ^ ((li >> 1) & 7));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        uo[j] = (wave * 16 + li) * 256 + 16 * ((4 * j + lg) ^ li);
+
+    const int64_t orow = (int64_t)Hv * DH;
+    constexpr int ES = OUT == DT_F32 || OUT == kOutNorm ? 4 : 2;
+    const uint32_t lane_off = (uint32_t)((4 * lg * orow + dvl) * ES);
+    f32x4 Oprev[4];
     int prev_tok0 = 0, prev_n = 0;
 
-    for (int ci = 0; ci < nch; ++ci) {
-        // this chunk's copies (issued one iteration ago), older stores, LDS writes
+    auto step = [&](auto slot, int ci) {
+        constexpr int SL = decltype(slot)::value;
+        // this chunk's copies (issued one chunk ago) have landed in every wave,
+        // and every wave is done reading the slot the next copies overwrite
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        if (ci > 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = wave * 16 + lg * 4 + r;
-                if (t < prev_n)
-                    store_out<OUT>(p, ((int64_t)(prev_tok0 + t) * Hv + h) * DH + dv0 + li,
-                                   hc.scale * Oprev[r]);
-            }
-        }
+        if (ci > 0)
+            store_rows<OUT>(p, prev_tok0, prev_n, h, orow, lane_off, lg, Oprev);
         if (ci + 1 < nch)
-            issue_chunk_copy<NW, 1>(img[(ci + 1) & 1], p, c0 + ci + 1, h, kh, dv0, wave, lane);
-        const ChunkImage<1> &cur = img[ci & 1];
-        const int sb = ci & 1;
+            issue_chunk_copy<NW, NW>(img[SL ^ 1], p, co, c0 + ci + 1, h, kh, dvw, wave, lane);
+        const ChunkImage<NW> &cur = img[SL];
+        // The phases below are kept in source order (scheduling fences) so that
+        // each phase's LDS operand reads are in flight during the previous
+        // phase's products instead of being issued just before their use.
 
-        // P = W S0^T and QS = Q S0^T for token rows 16w..16w+15
-        f32x4 P = {0.f, 0.f, 0.f, 0.f}, QS = {0.f, 0.f, 0.f, 0.f};
-        const int trow = wave * 16 + li;
+        // phase 1: operands of P' = W S^T - U, decay rows; the state as B operand
+        half8 wa[4][4];
+        f32x4 Pn[4], er[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const half8 b = lds_half8(&Sh[sb][li][ks * 32 + lg * 8]);
-            P = mfma16(img_read(cur.w, swz256(trow, 4 * ks + lg)), b, P);
-            QS = mfma16(img_read(cur.q, swz256(trow, 4 * ks + lg)), b, QS);
-        }
-        // D = U - P; the decayed D as an f16 hi + lo pair; gamma QS
-        f32x4 O;
+        for (int j = 0; j < 4; ++j) {
+            Pn[j] = img_f32x4(cur.u, uo[j]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = wave * 16 + lg * 4 + r;
-            const float d = cur.u[t][li] - P[r];
-            const float ds = d * cur.gd[C + t];
-            const _Float16 dh = (_Float16)ds;
-            const int tp = perm_pos(t);
-            DTl[li][tp] = (_Float16)d;
-            DsH[li][tp] = dh;
-            DsL[li][tp] = (_Float16)(ds - (float)dh);
-            O[r] = cur.gd[t] * QS[r];
+            for (int ks = 0; ks < 4; ++ks)
+                wa[j][ks] = img_half8(cur.w, wq[ks] + j * 4096);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            er[j] = *reinterpret_cast<const f32x4 *>(&cur.gd[C + 16 * j + 4 * lg]);
+        const f32x4 g3 = *reinterpret_cast<const f32x4 *>(&cur.gd[48 + 4 * lg]);
+        half8 sb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            sb[ks] = pack_tiles(ST[2 * ks], ST[2 * ks + 1]);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // O += Aqk D (only the token blocks at or below this wave's rows)
+        // phase 2: P' products, with the state update's K^T operands read behind them
+        half8 kb[8][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            if (2 * ks <= wave)
-                O = mfma16(img_read(cur.aq, swz128(trow, 4 * ks + lg)),
-                           lds_half8(&DTl[li][ks * 32 + lg * 8]), O);
-        // S_n = gamma_last S0 + D~^T K
-        const float gn = cur.gd[C - 1];
+        for (int i = 0; i < 16; ++i) {
+            const int j = i >> 2, ks = i & 3;
+            Pn[j] = mfma16(wa[j][ks], sb[ks], Pn[j]);
+            kb[i >> 1][i & 1] = img_half8(cur.kt, ka[i & 1] + (i >> 1) * 2048);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // phase 3: -D as hi + lo (for the output), D e as hi + lo (for the state)
+        half8 dn[2], dnl[2], dh[2], dl[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            S[nt] *= gn;
-            const int krow = wave * 32 + nt * 16 + li;
+        for (int ks = 0; ks < 2; ++ks) {
+            const f32x4 a = Pn[2 * ks] * er[2 * ks], b = Pn[2 * ks + 1] * er[2 * ks + 1];
+            dn[ks] = pack_tiles(Pn[2 * ks], Pn[2 * ks + 1]);
+            dh[ks] = pack_tiles(a, b);
+            f32x4 ar, br, pr, qr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ar[i] = a[i] - (float)dh[ks][i];
+                br[i] = b[i] - (float)dh[ks][4 + i];
+                pr[i] = Pn[2 * ks][i] - (float)dn[ks][i];
+                qr[i] = Pn[2 * ks + 1][i] - (float)dn[ks][4 + i];
+            }
+            dl[ks] = pack_tiles(ar, br);
+            dnl[ks] = pack_tiles(pr, qr);
+        }
+        // gamma_last = gamma_{C-1}: lane 48 holds it as the last entry of its row
+        const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g3[3]), 48));
+        __builtin_amdgcn_sched_barrier(0);
+
+        // phase 4: S^T <- gamma_last S^T + K^T (D e), with the output's operands read behind
+        half8 qa[4][4], aa[6];
+        f32x4 gm[4];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            ST[m] *= gl;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const half8 kb = img_read(cur.kt, swz128(krow, 4 * ks + lg));
-                S[nt] = mfma16(lds_half8(&DsH[li][ks * 32 + lg * 8]), kb, S[nt]);
-                S[nt] = mfma16(lds_half8(&DsL[li][ks * 32 + lg * 8]), kb, S[nt]);
+                ST[m] = mfma16(kb[m][ks], dh[ks], ST[m]);
+                ST[m] = mfma16(kb[m][ks], dl[ks], ST[m]);
+                const int i = 2 * m + ks;  // 16 Q reads, then Aqk and the gamma rows
+                qa[i >> 2][i & 3] = img_half8(cur.q, wq[i & 3] + (i >> 2) * 4096);
+                if (i < 6)
+                    aa[i] = img_half8(cur.aq, ka[i < 2 ? 0 : (i & 1)] + (i < 2 ? i : (i + 2) >> 1) * 2048);
+                if (i >= 6 && i < 10)
+                    gm[i - 6] = *reinterpret_cast<const f32x4 *>(&cur.gd[2 * C + 16 * (i - 6) + 4 * lg]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        Oprev = O;
+
+        // phase 5: O = scale gamma Q S^T + (-scale Aqk)(-D), off the state's chain
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qs = mfma16(qa[j][ks], sb[ks], qs);
+            qs *= gm[j];
+            // Aqk tiles (j, ks) with ks <= j / 2, in aa order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (2 * ks <= j) {
+                    const half8 &a = aa[j < 2 ? j : 2 + 2 * (j - 2) + ks];
+                    qs = mfma16(a, dn[ks], qs);
+                    qs = mfma16(a, dnl[ks], qs);
+                }
+            Oprev[j] = qs;
+        }
         prev_tok0 = start + ci * C;
         prev_n = min(C, len - ci * C);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Sh[sb ^ 1][lg * 4 + r][perm_pos(wave * 32 + nt * 16 + li)] = (_Float16)S[nt][r];
+    };
+
+    for (int ci = 0; ci < nch; ci += 2) {
+        step(Slot<0>{}, ci);
+        if (ci + 1 < nch)
+            step(Slot<1>{}, ci + 1);
     }
+    store_rows<OUT>(p, prev_tok0, prev_n, h, orow, lane_off, lg, Oprev);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = wave * 16 + lg * 4 + r;
-        if (t < prev_n)
-            store_out<OUT>(p, ((int64_t)(prev_tok0 + t) * Hv + h) * DH + dv0 + li,
-                           hc.scale * Oprev[r]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Sg[(int64_t)(dv0 + lg * 4 + r) * DH + wave * 32 + nt * 16 + li] = S[nt][r];
+    for (int m = 0; m < 8; ++m)
+        *reinterpret_cast<f32x4 *>(Sg + 16 * m) = ST[m];
 }
 
 // ---------------------------------------------------------------- 4. gated norm
@@ -745,14 +879,19 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
     case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
     }
+#ifndef GDN_CARRY_NW
+#define GDN_CARRY_NW 2
+#endif
+    constexpr int NW = GDN_CARRY_NW;  // dv slices (waves) per carry workgroup
     const int64_t groups = (int64_t)p.N * p.hc.Hv;
-    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / DT)));
+    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
+    const dim3 cblock(64 * NW);
     const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
     switch (omode) {
-    case kOutNorm: hipLaunchKernelGGL((carry_kernel<kOutNorm>), cgrid, dim3(256), 0, s, p); break;
-    case DT_F32: hipLaunchKernelGGL((carry_kernel<DT_F32>), cgrid, dim3(256), 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((carry_kernel<DT_F16>), cgrid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((carry_kernel<DT_BF16>), cgrid, dim3(256), 0, s, p); break;
+    case kOutNorm: hipLaunchKernelGGL((carry_kernel<NW, kOutNorm>), cgrid, cblock, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((carry_kernel<NW, DT_F32>), cgrid, cblock, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((carry_kernel<NW, DT_F16>), cgrid, cblock, 0, s, p); break;
+    default: hipLaunchKernelGGL((carry_kernel<NW, DT_BF16>), cgrid, cblock, 0, s, p); break;
     }
     if (p.hc.flags & F_GATED_NORM) {
         const int64_t rows = (int64_t)p.total * p.hc.Hv;
