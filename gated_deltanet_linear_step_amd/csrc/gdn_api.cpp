@@ -56,11 +56,11 @@ gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dty
     const int64_t v_w = (int64_t)d->num_v_heads * d->head_dim_v;
     if (in->q_stride < qk_w || in->k_stride < qk_w || in->v_stride < v_w)
         return GDN_ERR_SHAPE;
-    // q and k are read as groups of 4 elements: base and row stride must keep
+    // q, k and v are read as groups of 4 elements: base and row stride must keep
     // every group aligned to 4 elements.
     const int64_t es = dtype_size(in->qkv_dtype);
-    if (!aligned(in->q, 4 * es) || !aligned(in->k, 4 * es) || !aligned(in->v, es) ||
-        in->q_stride % 4 != 0 || in->k_stride % 4 != 0)
+    if (!aligned(in->q, 4 * es) || !aligned(in->k, 4 * es) || !aligned(in->v, 4 * es) ||
+        in->q_stride % 4 != 0 || in->k_stride % 4 != 0 || in->v_stride % 4 != 0)
         return GDN_ERR_ALIGN;
     if (d->flags & GDN_RAW_GATES) {
         if (!in->a || !in->b || !in->decay_param || !in->dt_bias)

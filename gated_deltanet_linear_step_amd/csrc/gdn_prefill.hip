@@ -160,12 +160,13 @@ template <int QT>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 {
     // LDS: X1 = normalised K rows (f16) then A / T (f32, in place);
-    //      X2 = normalised Q rows (f16) then the block-product scratch (f32).
+    //      X2 = normalised Q rows (f16), the block-product scratch (f32), then W (f16).
+    // K and Q rows are stored with dk in the permuted order, which W and Q keep.
     __shared__ __attribute__((aligned(16))) unsigned char X1[C * AP * 4];
     __shared__ __attribute__((aligned(16))) unsigned char X2[C * KP * 2];
-    __shared__ __attribute__((aligned(16))) _Float16 VbT[DH][TP];  // beta_t v_t, transposed
-    __shared__ __attribute__((aligned(16))) _Float16 KbT[DH][TP];  // beta_t gamma_t k_t, transposed
-    __shared__ float G_s[C], beta_s[C];
+    __shared__ __attribute__((aligned(16))) _Float16 VbT[DH][TP];  // beta_t v_t, [dv][token slot]
+    __shared__ __attribute__((aligned(16))) _Float16 KbT[DH][TP];  // beta_t gamma_t k_t, [dk slot][token slot]
+    __shared__ float G_s[C], beta_s[C], bg_s[C];
     static_assert(C * AP * 4 >= C * KP * 2, "X1 holds both the K rows and A / T");
     static_assert(C * KP * 2 >= 32 * 36 * 4, "X2 holds the Q rows and the 32x32 scratch");
 
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
         }
         G_s[lane] = G;  // tokens >= n carry G_{n-1} (their g is 0)
         beta_s[lane] = beta;
+        bg_s[lane] = beta * __expf(G);
     }
     __syncthreads();
 
@@ -251,27 +253,24 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
                                (_Float16)(kz.z - (float)kh4[2]), (_Float16)(kz.w - (float)kh4[3])};
             const half4 ql4 = {(_Float16)(qz.x - (float)qh4[0]), (_Float16)(qz.y - (float)qh4[1]),
                                (_Float16)(qz.z - (float)qh4[2]), (_Float16)(qz.w - (float)qh4[3])};
-            *reinterpret_cast<half4 *>(&Kh[t][c4]) = kh4;
-            *reinterpret_cast<half4 *>(&Qh[t][c4]) = qh4;
-            *reinterpret_cast<half4 *>(&Kl[t][c4]) = kl4;
-            *reinterpret_cast<half4 *>(&Ql[t][c4]) = ql4;
+            const int c4p = perm_pos(c4);  // the four stay adjacent
+            *reinterpret_cast<half4 *>(&Kh[t][c4p]) = kh4;
+            *reinterpret_cast<half4 *>(&Qh[t][c4p]) = qh4;
+            *reinterpret_cast<half4 *>(&Kl[t][c4p]) = kl4;
+            *reinterpret_cast<half4 *>(&Ql[t][c4p]) = ql4;
         }
     }
     __syncthreads();
 
-    // the v elements of the transposed tiles built after the products below:
-    // their loads are issued now so that the products hide their latency
-    constexpr int kTileIters = (DH * C / 8) / 256;
-    uint32_t vr[kTileIters][8];
+    // Transposed tiles are built after the products below by thread = (four
+    // adjacent dims dq, token octet o), the octet being token slots 8o .. 8o+7 of
+    // the permuted order; its v rows are loaded now so the products hide them.
+    const int dq = threadIdx.x & 31, oc = threadIdx.x >> 5;
+    Raw4<QT> vr[8];
 #pragma unroll
-    for (int it = 0; it < kTileIters; ++it) {
-        const int e = it * 256 + threadIdx.x;
-        const int j = e % DH, o = e / DH;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t r = tok0 + min(o * 8 + i, n - 1);
-            vr[it][i] = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DH + j);
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int t = perm_idx(8 * oc + i);
+        vr[i] = load_raw4<QT>(in.v, (int64_t)(tok0 + min(t, n - 1)) * in.v_stride + (int64_t)h * DH + 4 * dq);
     }
 
     // -- K K^T and Q K^T on the lower block triangle: wave w owns token rows 16w..
@@ -300,44 +299,50 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 
     __syncthreads();  // the remainders are dead: the transposed tiles take their space
 
-    // -- transposed tiles, one (dim, 8-token octet) item per 16-byte LDS write:
-    // beta v from the input (lanes along dim: coalesced), beta gamma k from the
-    // f16 rows just written (the same rounded K the gram and the carry use).
-#pragma unroll
-    for (int it = 0; it < kTileIters; ++it) {
-        const int e = it * 256 + threadIdx.x;
-        const int j = e % DH, o = e / DH;
-        half8 vb, kb;
+    // -- transposed tiles: beta v (dims natural) and beta gamma k (dims in slot
+    // order) as [dim][token slot]; the K^T the carry reads ([dk][token slot], dk
+    // natural) goes straight to the workspace from the same registers
+    {
+        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+        half8 vb[4], kb[4], kt[4];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int t = o * 8 + i;
-            const float bt = beta_s[t];  // 0 for tokens past the chunk's end
-            vb[i] = (_Float16)(bt * raw1_to_f32<QT>(vr[it][i]));
-            kb[i] = (_Float16)(bt * __expf(G_s[t]) * (float)Kh[t][j]);
+            const int t = perm_idx(8 * oc + i);
+            const float4 vf = raw4_to_f32<QT>(vr[i]);
+            const float bt = beta_s[t], bgt = bg_s[t];  // 0 for tokens past the chunk's end
+            const half4 kq = *reinterpret_cast<const half4 *>(&Kh[t][4 * dq]);
+            vb[0][i] = (_Float16)(bt * vf.x);
+            vb[1][i] = (_Float16)(bt * vf.y);
+            vb[2][i] = (_Float16)(bt * vf.z);
+            vb[3][i] = (_Float16)(bt * vf.w);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                kb[d][i] = (_Float16)(bgt * (float)kq[d]);
+                kt[d][i] = kq[d];
+            }
         }
-        *reinterpret_cast<half8 *>(&VbT[j][o * 8]) = vb;
-        *reinterpret_cast<half8 *>(&KbT[j][o * 8]) = kb;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            *reinterpret_cast<half8 *>(&VbT[4 * dq + d][8 * oc]) = vb[d];
+            *reinterpret_cast<half8 *>(&KbT[4 * dq + d][8 * oc]) = kb[d];
+        }
+        if (qk_writer) {
+            uint16_t *kdst = p.knT + ((int64_t)chunk * Hk + kh) * DH * C;
+            const int dk0 = perm_idx(4 * dq);  // slots 4dq .. 4dq+3 hold dk0 .. dk0+3
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                *reinterpret_cast<half8 *>(kdst + (dk0 + d) * C + 8 * oc) = kt[d];
+        }
     }
 
-    // normalised Q rows and K^T go to the workspace for the carry
+    // normalised Q rows (dk already in slot order) go to the workspace
     if (qk_writer) {
         uint16_t *qdst = p.qn + ((int64_t)chunk * Hk + kh) * C * DH;
-        uint16_t *kdst = p.knT + ((int64_t)chunk * Hk + kh) * DH * C;
-        for (int e = threadIdx.x; e < C * DH / 8; e += 256) {
+#pragma unroll
+        for (int k = 0; k < (C * DH / 8) / 256; ++k) {
+            const int e = k * 256 + threadIdx.x;
             const int t = e / (DH / 8), c8 = (e % (DH / 8)) * 8;
-            half8 v;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = Qh[t][perm_idx(c8 + i)];
-            *reinterpret_cast<half8 *>(qdst + t * DH + c8) = v;
-        }
-        for (int e = threadIdx.x; e < DH * C / 8; e += 256) {
-            const int dk = e % DH, t8 = (e / DH) * 8;
-            half8 v;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = Kh[perm_idx(t8 + i)][dk];
-            *reinterpret_cast<half8 *>(kdst + dk * C + t8) = v;
+            *reinterpret_cast<half8 *>(qdst + t * DH + c8) = lds_half8(&Qh[t][c8]);
         }
     }
     __syncthreads();  // Kh / Qh are dead from here: X1 becomes A / T, X2 scratch
@@ -423,16 +428,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     }
     __syncthreads();
 
-    // -- U = T (beta V) and W = T (beta gamma K): wave w owns token rows 16w..
+    // -- U = T (beta V) and W = T (beta gamma K): wave w owns token rows 16w..;
+    // the contraction runs over token slots, so T's columns are taken in slot order
     {
         half8 ta[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                ta[ks][i] = (_Float16)Am[wave * 16 + li][ks * 32 + lg * 8 + i];
+                ta[ks][i] = (_Float16)Am[wave * 16 + li][perm_idx(ks * 32 + lg * 8 + i)];
         float *ud = p.umat + ((int64_t)chunk * Hv + h) * DH * C;
-        uint16_t *wd = p.wmat + ((int64_t)chunk * Hv + h) * C * DH;
+        _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);  // W rows, staged
 #pragma unroll
         for (int nt = 0; nt < DH / 16; ++nt) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
@@ -444,10 +450,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             // -U^T: this lane's four tokens are adjacent in row dv
             *reinterpret_cast<f32x4 *>(ud + (nt * 16 + li) * C + wave * 16 + lg * 4) = -u;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = wave * 16 + lg * 4 + r;
-                wd[t * DH + perm_pos(nt * 16 + li)] = f32_to_f16_bits(w[r]);
-            }
+            for (int r = 0; r < 4; ++r)
+                Wl[wave * 16 + lg * 4 + r][nt * 16 + li] = (_Float16)w[r];
         }
     }
     if (threadIdx.x < C) {
@@ -460,6 +464,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
         gd[C + threadIdx.x] = -__expf(G_s[C - 1] - G_s[threadIdx.x]);
         gd[2 * C + threadIdx.x] = hc.scale * gm;
         gd[3 * C + threadIdx.x] = 0.f;
+    }
+    __syncthreads();
+    {
+        uint16_t *wd = p.wmat + ((int64_t)chunk * Hv + h) * C * DH;
+        _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);
+#pragma unroll
+        for (int k = 0; k < (C * DH / 8) / 256; ++k) {
+            const int e = k * 256 + threadIdx.x;
+            const int t = e / (DH / 8), c8 = (e % (DH / 8)) * 8;
+            *reinterpret_cast<half8 *>(wd + t * DH + c8) = lds_half8(&Wl[t][c8]);
+        }
     }
 }
 

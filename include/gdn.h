@@ -95,7 +95,9 @@ typedef struct gdn_dims {
  * decode step (sequence b, token t of T) and the packed token index for the
  * prefill. Element (row r, head, i) of q is at q[r * q_stride + head * dk + i]
  * (same for k with k_stride, v with v_stride and dv), so q, k, v may be strided
- * views into one mixed [tokens][2*Hk*dk + Hv*dv] row. Strides are in elements. */
+ * views into one mixed [tokens][2*Hk*dk + Hv*dv] row. Strides are in elements.
+ * The kernels read q, k and v in groups of 4 elements: each base pointer must be
+ * aligned to 4 elements and each stride a multiple of 4 (else GDN_ERR_ALIGN). */
 typedef struct gdn_inputs {
     const void *q, *k, *v;
     int64_t q_stride, k_stride, v_stride;

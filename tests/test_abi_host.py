@@ -96,6 +96,8 @@ def test_decode_validation():
     assert decode(inp=inputs(q_stride=100)) == SHAPE        # narrower than Hk*dk
     assert decode(inp=inputs(q=vp(P16 + 2))) == ALIGN       # not 4-element aligned
     assert decode(inp=inputs(k_stride=1026)) == ALIGN
+    assert decode(inp=inputs(v=vp(P16 + 2))) == ALIGN       # v is read in groups of 4 too
+    assert decode(inp=inputs(v_stride=2050)) == ALIGN
     assert decode(state=P16 + 4) == ALIGN                   # state needs 16 bytes
     assert decode(T=0) == SHAPE
     assert decode(batch=-1) == SHAPE
