@@ -226,6 +226,54 @@ gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_p
     return launch_status(gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_decode_layer(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
+                            const gdn_conv_args *conv, const gdn_inputs *in, float *state,
+                            const int32_t *state_slots, int32_t num_slots, int32_t out_dtype,
+                            void *out, void *stream)
+{
+    gdn::DecodeParams p{};
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::decode_supported, p.hc, p.in);
+    if (st != GDN_OK)
+        return st;
+    if (!conv || !conv->weight || !conv->state_in || !conv->state_out)
+        return GDN_ERR_NULL;
+    if (conv->kernel_size != 4)
+        return GDN_ERR_UNSUPPORTED;  // the built conv width
+    if (batch < 0 || tokens_per_seq < 1 || num_slots < 0)
+        return GDN_ERR_SHAPE;
+    if (!state_slots && num_slots < batch)
+        return GDN_ERR_SHAPE;
+    if ((int64_t)batch * tokens_per_seq > kI32Max || (int64_t)batch * dims->num_v_heads > kI32Max)
+        return GDN_ERR_OVERFLOW;
+    const int64_t es = dtype_size(in->qkv_dtype);
+    if (!aligned(conv->weight, 4 * es) || !aligned(conv->state_in, 4 * es) ||
+        !aligned(conv->state_out, 4 * es))
+        return GDN_ERR_ALIGN;
+    // the new window goes to a second buffer (the q/k channels of a k-head are
+    // read by several workgroups), so the two may not overlap
+    const int64_t channels = 2 * (int64_t)dims->num_k_heads * dims->head_dim_k +
+                             (int64_t)dims->num_v_heads * dims->head_dim_v;
+    const int64_t sbytes = (int64_t)num_slots * channels * (conv->kernel_size - 1) * es;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(conv->state_in);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(conv->state_out);
+    if (sbytes > 0 && a0 < b0 + (uintptr_t)sbytes && b0 < a0 + (uintptr_t)sbytes)
+        return GDN_ERR_SHAPE;
+    if (batch == 0)
+        return GDN_OK;
+    p.state = state;
+    p.slots = state_slots;
+    p.num_slots = num_slots;
+    p.out = out;
+    p.out_dt = out_dtype;
+    p.B = batch;
+    p.T = tokens_per_seq;
+    p.conv_k = conv->kernel_size;
+    p.conv_w = conv->weight;
+    p.conv_in = conv->state_in;
+    p.conv_out = conv->state_out;
+    return launch_status(gdn::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_prefill_workspace_bytes(const gdn_dims *d, int32_t num_seqs, int32_t total_tokens)
 {
     if (!d || num_seqs < 0 || total_tokens < 0 || d->num_k_heads < 1 || d->num_v_heads < 1 ||

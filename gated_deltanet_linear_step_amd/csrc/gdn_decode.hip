@@ -24,6 +24,12 @@
 //    arrives one element per lane and is spread to the rows by shuffles. The
 //    outputs are gathered in LDS and the gated RMS norm runs over them after
 //    each group of tokens.
+//  * CK > 0 (gdn_decode_layer): q, k, v arrive before the causal conv. Thread c
+//    of the workgroup owns one of the 2 dk + dv channels it reads (its weights
+//    and the window of the last CK-1 raw inputs in registers), convolves a group
+//    of tokens into LDS, and the waves take q, k, v from there. The window after
+//    the call goes to the output conv state; q/k channels are written by one
+//    workgroup per k-head.
 
 #include "gdn_device.h"
 #include "gdn_kernels.h"
@@ -74,22 +80,61 @@ struct TokenRaw {
     uint32_t ga, gb, v;
 };
 
-template <int DK, int DV, int QT>
+template <int DK, int DV, int QT, bool QKV = true>
 __device__ __forceinline__ void load_token(TokenRaw<QT> &t, const DecodeParams &p, int64_t r,
                                            int h, int kh, int col, int vrow)
 {
     const ActInputs &in = p.in;
     const int Hv = p.hc.Hv;
-    t.k = load_raw4<QT>(in.k, r * in.k_stride + (int64_t)kh * DK + col);
-    t.q = load_raw4<QT>(in.q, r * in.q_stride + (int64_t)kh * DK + col);
+    if constexpr (QKV) {
+        t.k = load_raw4<QT>(in.k, r * in.k_stride + (int64_t)kh * DK + col);
+        t.q = load_raw4<QT>(in.q, r * in.q_stride + (int64_t)kh * DK + col);
+    }
     const bool raw = p.hc.flags & F_RAW_GATES;
     const int gdt = raw ? in.ab_dt : DT_F32;
     t.ga = load_word_nb(raw ? in.a : (const void *)in.g, r * Hv + h, gdt);
     t.gb = load_word_nb(raw ? in.b : (const void *)in.beta, r * Hv + h, gdt);
-    t.v = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DV + vrow);
+    if constexpr (QKV)
+        t.v = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DV + vrow);
 }
 
-template <int DK, int DV, int NW, int QT>
+// The causal conv of one channel for the fused layer: weights and the window of
+// the last CK-1 raw inputs (oldest first) in registers. w[0] pairs with the
+// oldest input.
+template <int QT, int CK>
+struct ConvLane {
+    float w[CK], win[CK - 1];
+
+    __device__ __forceinline__ void load(const DecodeParams &p, int64_t ch, int64_t sbase)
+    {
+#pragma unroll
+        for (int m = 0; m < CK; ++m)
+            w[m] = raw1_to_f32<QT>(load_raw1<QT>(p.conv_w, ch * CK + m));
+#pragma unroll
+        for (int m = 0; m < CK - 1; ++m)
+            win[m] = raw1_to_f32<QT>(load_raw1<QT>(p.conv_in, sbase + m));
+    }
+    __device__ __forceinline__ float tap(float x)
+    {
+        float acc = w[CK - 1] * x;
+#pragma unroll
+        for (int m = 0; m < CK - 1; ++m)
+            acc = fmaf(w[m], win[m], acc);
+#pragma unroll
+        for (int m = 0; m < CK - 2; ++m)
+            win[m] = win[m + 1];
+        win[CK - 2] = x;
+        return silu_f(acc);
+    }
+    __device__ __forceinline__ void store(const DecodeParams &p, int64_t sbase) const
+    {
+#pragma unroll
+        for (int m = 0; m < CK - 1; ++m)
+            store_act(p.conv_out, sbase + m, QT, win[m]);
+    }
+};
+
+template <int DK, int DV, int NW, int QT, int CK>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
 {
     constexpr int LPR = DK / 4;       // lanes holding one row
@@ -100,6 +145,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     static_assert(RPW <= 64, "one v value per lane covers the wave's rows");
 
     __shared__ float o_s[kTokGroup][DV];
+    constexpr int NCH = 2 * DK + DV;  // conv channels one workgroup reads
+    static_assert(CK == 0 || NCH <= NW * 64, "one conv channel per thread");
+    __shared__ float y_s[CK > 0 ? kTokGroup : 1][CK > 0 ? NCH : 1];  // conv outputs
 
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv;
@@ -128,7 +176,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     // are counted in order, so the prologue math can run while the state is in
     // flight, and each row piece is processed as soon as it lands.
     TokenRaw<QT> tr;
-    load_token<DK, DV, QT>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
+    load_token<DK, DV, QT, CK == 0>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
+    // fused conv: this thread's channel (q, k or v), its raw input of the first
+    // token group, weights and window, all issued before the state loads
+    const int64_t nch = 2 * (int64_t)hc.Hk * DK + (int64_t)Hv * DV;
+    const int cl = threadIdx.x;  // channel within the workgroup's 2 dk + dv
+    int64_t cch = 0;             // its index in the conv channel order
+    const void *xsrc = nullptr;
+    int64_t xoff = 0, xstride = 0;
+    ConvLane<QT, (CK > 0 ? CK : 2)> cvl;
+    uint32_t xr[kTokGroup];
+    if constexpr (CK > 0) {
+        if (cl < DK) {
+            cch = (int64_t)kh * DK + cl;
+            xsrc = p.in.q; xoff = (int64_t)kh * DK + cl; xstride = p.in.q_stride;
+        } else if (cl < 2 * DK) {
+            cch = (int64_t)hc.Hk * DK + (int64_t)kh * DK + (cl - DK);
+            xsrc = p.in.k; xoff = (int64_t)kh * DK + (cl - DK); xstride = p.in.k_stride;
+        } else {
+            cch = 2 * (int64_t)hc.Hk * DK + (int64_t)h * DV + (cl - 2 * DK);
+            xsrc = p.in.v; xoff = (int64_t)h * DV + (cl - 2 * DK); xstride = p.in.v_stride;
+        }
+        if (cl < NCH) {
+            cvl.load(p, cch, ((int64_t)slot * nch + cch) * (CK - 1));
+            const int tn = min(p.T, kTokGroup);
+#pragma unroll
+            for (int tt = 0; tt < kTokGroup; ++tt)
+                if (tt < tn)
+                    xr[tt] = load_raw1<QT>(xsrc, ((int64_t)b * p.T + tt) * xstride + xoff);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the token loads ahead of the state loads
 
     float *Sg = p.state + ((int64_t)slot * Hv + h) * (int64_t)(DV * DK);
@@ -138,13 +215,47 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
         S[i] = load_state4(Sg + (row0 + i * RPI) * DK + col);
     __builtin_amdgcn_sched_barrier(0);  // ... and their use behind the state loads
     const bool raw_gates = flags & F_RAW_GATES;
+
+    // fused conv of tokens [t0, t0 + tn) into y_s (xr holds their raw inputs)
+    auto conv_group = [&](int tn) {
+        if constexpr (CK > 0) {
+            if (cl < NCH) {
+                for (int tt = 0; tt < tn; ++tt)
+                    y_s[tt][cl] = cvl.tap(raw1_to_f32<QT>(xr[tt]));
+            }
+        }
+    };
+    auto load_group = [&](int t0, int tn) {
+        if constexpr (CK > 0) {
+            if (cl < NCH) {
+#pragma unroll
+                for (int tt = 0; tt < kTokGroup; ++tt)
+                    if (tt < tn)
+                        xr[tt] = load_raw1<QT>(xsrc, ((int64_t)b * p.T + t0 + tt) * xstride + xoff);
+            }
+        }
+    };
+    if constexpr (CK > 0) {
+        conv_group(min(p.T, kTokGroup));
+        __syncthreads();
+    }
     const int gdt = raw_gates ? p.in.ab_dt : DT_F32;
 
     // One token through this wave's rows: prologue (norms, gates), then the two
     // reductions, the update and the read-out per row piece; outputs go to
     // o_s[tt] for the group epilogue.
     auto process_token = [&](int tt, int64_t r) {
-        float4 kk = raw4_to_f32<QT>(tr.k), qq = raw4_to_f32<QT>(tr.q);
+        float4 kk, qq;
+        float vv;
+        if constexpr (CK > 0) {
+            qq = *reinterpret_cast<const float4 *>(&y_s[tt][col]);
+            kk = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col]);
+            vv = y_s[tt][2 * DK + vrow];
+        } else {
+            kk = raw4_to_f32<QT>(tr.k);
+            qq = raw4_to_f32<QT>(tr.q);
+            vv = raw1_to_f32<QT>(tr.v);
+        }
         if (flags & F_L2NORM) {
             const float sk = group_sum<LPR>(dot4(kk, kk));
             const float sq = group_sum<LPR>(dot4(qq, qq));
@@ -164,7 +275,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
         }
         const float alpha = expf(g);
         const float kq = group_sum<LPR>(dot4(kk, qq));
-        const float vv = raw1_to_f32<QT>(tr.v);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const float pk = group_sum<LPR>(dot4(S[i], kk));
@@ -208,32 +318,49 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     process_token(0, (int64_t)b * p.T);
     for (int t = 1; t < p.T; ++t) {
         const int tt = t % kTokGroup;
-        if (tt == 0) {  // o_s holds a full group: drain it
+        if (tt == 0) {  // o_s (and y_s) hold a full group: drain it, convolve the next
+            load_group(t, min(p.T - t, kTokGroup));
             __syncthreads();
             epilogue(t - kTokGroup, kTokGroup);
+            conv_group(min(p.T - t, kTokGroup));
             __syncthreads();
         }
         const int64_t r = (int64_t)b * p.T + t;
-        load_token<DK, DV, QT>(tr, p, r, h, kh, col, vrow);
+        load_token<DK, DV, QT, CK == 0>(tr, p, r, h, kh, col, vrow);
         process_token(tt, r);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         store_state4(Sg + (row0 + i * RPI) * DK + col, S[i]);
+    if constexpr (CK > 0) {
+        // the window after this call's tokens; q/k channels from one v-head per k-head
+        const bool qk_writer = hc.head_map == 0 ? (h % (Hv / hc.Hk) == 0) : (h < hc.Hk);
+        if (cl < NCH && (cl >= 2 * DK || qk_writer))
+            cvl.store(p, ((int64_t)slot * nch + cch) * (CK - 1));
+    }
     __syncthreads();
     const int tlast0 = ((p.T - 1) / kTokGroup) * kTokGroup;
     epilogue(tlast0, p.T - tlast0);
 }
 
-template <int DK, int DV, int NW>
-hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
+template <int DK, int DV, int NW, int CK>
+void launch_decode_ck(const DecodeParams &p, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)p.B * p.hc.Hv)), block(NW * 64);
     switch (p.in.qkv_dt) {
-    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32>), grid, block, 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16>), grid, block, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK>), grid, block, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK>), grid, block, 0, s, p); break;
     }
+}
+
+template <int DK, int DV, int NW>
+hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
+{
+    if (p.conv_k == 4)
+        launch_decode_ck<DK, DV, NW, 4>(p, s);
+    else
+        launch_decode_ck<DK, DV, NW, 0>(p, s);
     return hipGetLastError();
 }
 

@@ -37,6 +37,11 @@ struct DecodeParams {
     void *out;
     int out_dt;
     int B, T;
+    // gdn_decode_layer: q/k/v are pre-conv; conv_k > 0 applies the causal conv
+    // (weights [channels][K], state [slots][channels][K-1], ping-pong in/out)
+    int conv_k;
+    const void *conv_w, *conv_in;
+    void *conv_out;
 };
 
 struct ConvParams {

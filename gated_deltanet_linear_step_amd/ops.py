@@ -27,7 +27,7 @@ L2NORM_QK, RAW_GATES, GATED_NORM = 1, 2, 4
 CHUNK = 64
 
 EXPORTED = ["gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
-            "gdn_prefill_chunked", "gdn_status_string", "gdn_version"]
+            "gdn_prefill_chunked", "gdn_status_string", "gdn_version", "gdn_decode_layer"]
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _VP = ctypes.c_void_p
@@ -49,6 +49,11 @@ class Inputs(ctypes.Structure):
                 ("decay_param", _VP), ("dt_bias", _VP),
                 ("g", _VP), ("beta", _VP),
                 ("z", _VP), ("z_dtype", ctypes.c_int32), ("norm_weight", _VP)]
+
+
+class ConvArgs(ctypes.Structure):
+    _fields_ = [("kernel_size", ctypes.c_int32), ("weight", _VP), ("state_in", _VP),
+                ("state_out", _VP)]
 
 
 class GdnError(RuntimeError):
@@ -81,6 +86,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(Inputs), _VP, _VP, ctypes.c_int32,
                                     ctypes.c_int32, _VP, _VP]
+    lib.gdn_decode_layer.restype = ctypes.c_int
+    lib.gdn_decode_layer.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.POINTER(ConvArgs), ctypes.POINTER(Inputs), _VP, _VP,
+                                     ctypes.c_int32, ctypes.c_int32, _VP, _VP]
     lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32,
                                                 ctypes.c_int32]
@@ -227,6 +236,40 @@ def decode_step(q, k, v, state, *, Hk, Hv, dk, dv, head_map, batch, tokens_per_s
     return out
 
 
+def decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_out, *, Hk, Hv, dk, dv,
+                 head_map, batch, tokens_per_seq=1, a=None, b=None, decay_param=None,
+                 dt_bias=None, g=None, beta=None, z=None, norm_weight=None, l2norm_qk=True,
+                 decay=DECAY_LOG_RATE, scale=0.0, state_slots=None, out=None,
+                 out_dtype=torch.float32, stream=None):
+    """One call of gdn_decode_layer: q, k, v are the pre-conv projections (views of
+    the mixed row allowed); conv_weight [channels][4], conv states [slots][channels][3]
+    in q's dtype (read from conv_state_in, the new window written to conv_state_out);
+    state [slots][Hv][dv][dk] f32 updated in place. Returns out [B*T][Hv][dv]."""
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be contiguous float32")
+    for name, t in (("conv_weight", conv_weight), ("conv_state_in", conv_state_in),
+                    ("conv_state_out", conv_state_out)):
+        if t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous in q's dtype")
+    conv = ConvArgs(conv_weight.shape[1], _ptr(conv_weight), _ptr(conv_state_in),
+                    _ptr(conv_state_out))
+    rows = batch * tokens_per_seq
+    if out is None:
+        out = torch.empty((rows, Hv, dv), dtype=out_dtype, device=state.device)
+    st = load().gdn_decode_layer(ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(conv),
+                                 ctypes.byref(inp), _ptr(state), _ptr(state_slots), state.shape[0],
+                                 _dt(out), _ptr(out), _stream(stream))
+    _check(st, "gdn_decode_layer")
+    del keep
+    return out
+
+
 def prefill_workspace_bytes(*, Hk, Hv, dk, dv, head_map=MAP_GROUPED, num_seqs, total_tokens):
     dims = make_dims(Hk, Hv, dk, dv, head_map, 0)
     return int(load().gdn_prefill_workspace_bytes(ctypes.byref(dims), num_seqs, total_tokens))
@@ -302,6 +345,26 @@ def prepare_decode_step(q, k, v, state, out, *, Hk, Hv, dk, dv, head_map, batch,
             _ptr(state_slots), state.shape[0], _dt(out), _ptr(out), _stream(stream))
     return PreparedCall(load().gdn_decode_step, args, "gdn_decode_step",
                         keep + [dims, inp, state, out, state_slots])
+
+
+def prepare_decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_out, out, *, Hk,
+                         Hv, dk, dv, head_map, batch, tokens_per_seq=1, a=None, b=None,
+                         decay_param=None, dt_bias=None, g=None, beta=None, z=None,
+                         norm_weight=None, l2norm_qk=True, decay=DECAY_LOG_RATE, scale=0.0,
+                         state_slots=None, stream=None) -> PreparedCall:
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    conv = ConvArgs(conv_weight.shape[1], _ptr(conv_weight), _ptr(conv_state_in),
+                    _ptr(conv_state_out))
+    args = (ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(conv), ctypes.byref(inp),
+            _ptr(state), _ptr(state_slots), state.shape[0], _dt(out), _ptr(out), _stream(stream))
+    return PreparedCall(load().gdn_decode_layer, args, "gdn_decode_layer",
+                        keep + [dims, inp, conv, state, out, state_slots, conv_weight,
+                                conv_state_in, conv_state_out])
 
 
 def prepare_prefill_chunked(q, k, v, state, cu_seqlens_dev, cu_seqlens_host, out, workspace, *,

@@ -167,6 +167,42 @@ gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_p
                            const gdn_inputs *in, float *state, const int32_t *state_slots,
                            int32_t num_slots, int32_t out_dtype, void *out, void *stream);
 
+/* The causal conv that gdn_decode_layer applies to q, k and v before the
+ * recurrence: the same operation as gdn_conv_update over the channel order
+ * [q (Hk*dk) | k (Hk*dk) | v (Hv*dv)] of the mixed projection row. */
+typedef struct gdn_conv_args {
+    int32_t kernel_size;  /* K; the built layer kernel supports K = 4 */
+    const void *weight;   /* [channels][K] in the activations' dtype (qkv_dtype) */
+    const void *state_in; /* [num_slots][channels][K-1], oldest first, qkv_dtype */
+    void *state_out;      /* same shape; must not overlap state_in */
+} gdn_conv_args;
+
+/* ---------------------------------------------------------------------------
+ * gdn_decode_layer -- one launch for the whole decode layer: causal conv + SiLU
+ * of q, k, v with carried raw inputs (ferrum-kernels tests page, `cpu_segment`
+ * conv section; libmir-metal decode/mod.rs `convolve`), then everything
+ * gdn_decode_step does (L2 norm, gates, recurrence, gated norm).
+ *
+ * Arguments are those of gdn_decode_step, except:
+ *   in->q, in->k, in->v  the PRE-conv projections (e.g. views into the mixed
+ *                        [tokens][2*Hk*dk + Hv*dv] row)
+ *   conv                 weights and conv state; the state is indexed by the
+ *                        same slot as the delta state. The call reads state_in
+ *                        and writes the window after its tokens to state_out
+ *                        (a caller alternates two buffers); both must be aligned
+ *                        to 4 elements. A slot outside [0, num_slots) leaves both
+ *                        states and the output rows untouched.
+ * Every v-head workgroup computes the conv of the q/k channels it reads; the
+ * new q/k window is written by one workgroup per k-head, which is why the
+ * state is not updated in place.
+ * Errors: those of gdn_decode_step; NULL (conv pointers), UNSUPPORTED (K),
+ * ALIGN (conv buffers), SHAPE (state_out overlapping state_in).
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_decode_layer(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
+                            const gdn_conv_args *conv, const gdn_inputs *in, float *state,
+                            const int32_t *state_slots, int32_t num_slots, int32_t out_dtype,
+                            void *out, void *stream);
+
 /* ---------------------------------------------------------------------------
  * gdn_prefill_workspace_bytes -- device workspace gdn_prefill_chunked needs for
  * at most num_seqs sequences and total_tokens packed tokens (an upper bound

@@ -157,3 +157,29 @@ def test_prefill_validation():
                                    None) == NULL
     zero = (ctypes.c_int32 * 3)(0, 0, 0)
     assert call(cu=zero, total=0) == OK    # all sequences empty: nothing launched
+
+
+def test_layer_validation():
+    lib = ops.load()
+    sbytes = 2 * (2 * 2 * 128 + 4 * 128) * 3 * 2  # num_slots=2, channels, K-1, bf16
+
+    def layer(d=None, K=4, w=P16, cin=P16, cout=P16 + sbytes, batch=0, T=1, num_slots=2,
+              inp=None, state=P16, out=P16):
+        d = dims() if d is None else d
+        inp = inputs() if inp is None else inp
+        ca = ops.ConvArgs(K, vp(w) if w else None, vp(cin) if cin else None,
+                          vp(cout) if cout else None)
+        return lib.gdn_decode_layer(ctypes.byref(d), batch, T, ctypes.byref(ca), ctypes.byref(inp),
+                                    vp(state), None, num_slots, 0, vp(out), None)
+
+    assert layer() == OK                                    # batch 0: nothing launched
+    assert layer(w=0) == NULL and layer(cin=0) == NULL and layer(cout=0) == NULL
+    assert lib.gdn_decode_layer(ctypes.byref(dims()), 0, 1, None, ctypes.byref(inputs()),
+                                vp(P16), None, 2, 0, vp(P16), None) == NULL
+    assert layer(K=3) == UNSUPPORTED and layer(K=5) == UNSUPPORTED  # built for K = 4
+    assert layer(cin=P16 + 2) == ALIGN and layer(w=P16 + 6) == ALIGN
+    assert layer(cout=P16 + 256) == SHAPE                   # overlaps the input window
+    assert layer(cout=P16 - sbytes + 8) == SHAPE
+    assert layer(d=dims(Hk=3)) == SHAPE                     # the decode step's own checks
+    assert layer(T=0) == SHAPE
+    assert layer(inp=inputs(v_stride=2050)) == ALIGN

@@ -1,0 +1,140 @@
+"""GPU parity of gdn_decode_layer (conv + the whole decode step in one launch)
+against the CPU oracle, and against the two-launch path it replaces.
+
+Same bars as the decode contract: max-abs 1e-3 on outputs and states; the conv
+window is a carry of raw inputs and must match exactly; a T-token call and its
+3+1 split agree bit for bit; the call never writes its input conv state.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_step_amd import ops, synth
+from test_gpu_decode import DEV, TOL, f64, maxabs, oracle_layer, run_layer, to_dev, ulp16, \
+    layer_conformance_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(W, *, T, B, cs_in, cs_out, out_dtype=torch.float32, state=None, x=None, z=None,
+              a=None, b=None, slots=None, out=None):
+    Hk, Hv, dk, dv = W["Hk"], W["Hv"], W["dk"], W["dv"]
+    QK = Hk * dk
+    x = W["x_d"] if x is None else x
+    return ops.decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
+                            W["state_d"] if state is None else state, W["conv_w_d"], cs_in,
+                            cs_out, Hk=Hk, Hv=Hv, dk=dk, dv=dv, head_map=W["head_map"],
+                            batch=B, tokens_per_seq=T, a=W["a_d"] if a is None else a,
+                            b=W["b_d"] if b is None else b, decay_param=W["A_log_d"],
+                            dt_bias=W["dt_bias_d"], z=W["z_d"] if z is None else z,
+                            norm_weight=W["norm_w_d"], out_dtype=out_dtype, state_slots=slots,
+                            out=out)
+
+
+def test_fused_layer_conformance_fp16_split_and_oracle():
+    W = layer_conformance_workload()
+    cs0 = W["conv_state_d"].clone()
+    st_full, cs_out = W["state_d"].clone(), torch.empty_like(cs0)
+    out_full = run_fused(W, T=4, B=1, cs_in=cs0, cs_out=cs_out, state=st_full)
+    # 3 + 1 split, alternating the conv buffers
+    st_split, cs_a, cs_b = W["state_d"].clone(), cs0.clone(), torch.empty_like(cs0)
+    parts = []
+    for (lo, hi), (ci, co) in zip(((0, 3), (3, 4)), ((cs_a, cs_b), (cs_b, cs_a))):
+        sl = lambda t: t[lo:hi].contiguous()  # noqa: E731
+        parts.append(run_fused(W, T=hi - lo, B=1, cs_in=ci, cs_out=co, state=st_split,
+                               x=sl(W["x_d"]), z=sl(W["z_d"]), a=sl(W["a_d"]), b=sl(W["b_d"])))
+    torch.cuda.synchronize()
+    assert torch.equal(cs0, W["conv_state_d"]), "the input conv state was written"
+    assert torch.equal(out_full, torch.cat(parts)), "4-token call and 3+1 split differ"
+    assert torch.equal(st_full, st_split) and torch.equal(cs_out, cs_a)
+
+    y, cs, S = oracle_layer(W, B=1, T=4)
+    o = f64(out_full).reshape(y.shape)
+    assert np.any(np.abs(o) > 1e-4)
+    assert maxabs(o, y) <= TOL
+    assert maxabs(f64(st_full), S) <= TOL
+    assert maxabs(f64(cs_out), cs) == 0.0
+    # the two-launch path (conv_update + decode_step) on the same inputs
+    st2 = W["state_d"].clone()
+    out2 = run_layer(W, T=4, B=1, state=st2, conv_state=cs0.clone())
+    torch.cuda.synchronize()
+    assert maxabs(f64(out_full), f64(out2)) <= 1e-5
+    assert maxabs(f64(st_full), f64(st2)) <= 1e-6
+
+
+def test_fused_layer_b64_steps_1_and_8():
+    B = 64
+    W = to_dev(synth.decode_batch(seed=2, B=B, head_map=synth.TILED))
+    S_ref, cs_ref = f64(W["state"]), f64(W["conv_state"])
+    bufs = [W["conv_state_d"].clone(), torch.empty_like(W["conv_state_d"])]
+    for step in range(1, 9):
+        out = run_fused(W, T=1, B=B, cs_in=bufs[0], cs_out=bufs[1], out_dtype=torch.float32)
+        bufs.reverse()
+        y, cs_ref, S_ref = oracle_layer(W, B=B, T=1, state=S_ref, conv_state=cs_ref)
+        if step in (1, 8):
+            torch.cuda.synchronize()
+            assert maxabs(f64(out).reshape(y.shape), y) <= TOL, f"step {step} output"
+            assert maxabs(f64(W["state_d"]), S_ref) <= TOL, f"step {step} state"
+            assert maxabs(f64(bufs[0]), cs_ref) == 0.0, f"step {step} conv state"
+
+
+@pytest.mark.parametrize("d,Hk,Hv", [(128, 2, 4), (64, 2, 2), (32, 1, 4)])
+@pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
+@pytest.mark.parametrize("T", [1, 3, 9, 17])
+def test_fused_layer_shapes_maps_tokens(d, Hk, Hv, head_map, T):
+    B = 3
+    W = to_dev(synth.decode_batch(seed=40 + T + d, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d, T=T,
+                                  head_map=head_map))
+    cs_out = torch.full_like(W["conv_state_d"], 9.0)
+    out = run_fused(W, T=T, B=B, cs_in=W["conv_state_d"], cs_out=cs_out)
+    torch.cuda.synchronize()
+    y, cs, S = oracle_layer(W, B=B, T=T)
+    assert maxabs(f64(out).reshape(y.shape), y) <= TOL
+    assert maxabs(f64(W["state_d"]), S) <= TOL
+    assert maxabs(f64(cs_out), cs) == 0.0
+
+
+@pytest.mark.parametrize("act", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fused_layer_dtypes(act, out_dtype):
+    B, T = 4, 2
+    W = to_dev(synth.decode_batch(seed=51, B=B, Hk=2, Hv=4, T=T, dtype=act))
+    cs_out = torch.empty_like(W["conv_state_d"])
+    out = run_fused(W, T=T, B=B, cs_in=W["conv_state_d"], cs_out=cs_out, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    y, cs, S = oracle_layer(W, B=B, T=T)
+    o = f64(out).reshape(y.shape)
+    bound = TOL if out_dtype == torch.float32 else ulp16(y, out_dtype) + TOL
+    assert np.all(np.abs(o - y) <= bound)
+    assert maxabs(f64(W["state_d"]), S) <= TOL
+    assert maxabs(f64(cs_out), cs) == 0.0
+
+
+def test_fused_layer_slots_and_out_of_range_slot():
+    B, Hk, Hv, d, nslots = 3, 2, 4, 64, 5
+    W = to_dev(synth.decode_batch(seed=61, B=nslots, Hk=Hk, Hv=Hv, dk=d, dv=d))
+    slots = [4, 77, 1]
+    # activations of the three sequences; states and conv windows live in a pool of 5
+    x = W["x_d"][:B].contiguous()
+    z, a, b = W["z_d"][:B].contiguous(), W["a_d"][:B].contiguous(), W["b_d"][:B].contiguous()
+    pool0, cs_pool0 = W["state_d"].clone(), W["conv_state_d"].clone()
+    pool, cs_out = W["state_d"], torch.full_like(cs_pool0, 5.0)
+    out = torch.full((B, Hv, d), 7.0, device=DEV)
+    run_fused(W, T=1, B=B, cs_in=cs_pool0, cs_out=cs_out, x=x, z=z, a=a, b=b,
+              slots=torch.tensor(slots, dtype=torch.int32, device=DEV), out=out)
+    torch.cuda.synchronize()
+    for bi, s in enumerate(slots):
+        if s >= nslots:
+            assert torch.all(out[bi] == 7.0)
+            continue
+        Wi = dict(W)
+        for key in ("x", "z", "a", "b"):
+            Wi[key] = W[key][bi:bi + 1]
+        y, cs, S = oracle_layer(Wi, B=1, T=1, state=f64(pool0[s:s + 1]),
+                                conv_state=f64(cs_pool0[s:s + 1]))
+        assert maxabs(f64(out[bi:bi + 1]).reshape(y.shape), y) <= TOL
+        assert maxabs(f64(pool[s]), S[0]) <= TOL
+        assert maxabs(f64(cs_out[s]), cs[0]) == 0.0
+    for s in (0, 2, 3):  # slots no sequence named: both states untouched
+        assert torch.equal(pool[s], pool0[s])
+        assert torch.all(cs_out[s] == 5.0)
