@@ -4,21 +4,23 @@
 Default workload (the headline one): batched decode, B=64 independent sequences
 of one token each, Hk=16, Hv=32, dk=dv=128, tiled k-head map, bf16 activations
 drawn N(0,1), fp32 state N(0, 0.02^2), conv width 4 with carried state. One step
-is one pass of the whole decode path: gdn_conv_update (depthwise conv + SiLU,
-state carry) then gdn_decode_step (split, L2 norm of q/k, gates, recurrence,
-gated RMS norm fused). The same inputs are reused every step; the state evolves.
+is one pass of the whole decode path in one launch: gdn_decode_layer (depthwise
+conv + SiLU with the conv window carried between two buffers, split, L2 norm of
+q/k, gates, recurrence, gated RMS norm). The same inputs are reused every step;
+the state evolves.
 
 Metric: decode state GB/s = 2 * B * Hv * dv * dk * 4 bytes (the fp32 state read
 and written once) / step time, the definition of the ferrox-core gdn.rs
 throughput probe. Also reported on the same JSON line:
-  * roofline: the decode kernel's algorithmic bytes per launch / its average
-    duration (one HIP event pair around K back-to-back decode launches, timed
-    right after the K steps), against
-    the 8 TB/s HBM peak; traffic from the committed rocprofv3 FETCH/WRITE counter
-    summary when it was taken on the current kernel source, else null;
-  * rotating: the same step cycling through 4 independent state sets (537 MB,
+  * roofline: the layer kernel's algorithmic bytes per launch / its average
+    duration (one HIP event pair around K back-to-back launches, timed right
+    after the K steps), against the 8 TB/s HBM peak; traffic from the committed
+    rocprofv3 FETCH/WRITE counter summary when it was taken on the current
+    kernel source, else null;
+  * two_launch: the same step as gdn_conv_update then gdn_decode_step;
+  * rotating: the step cycling through 4 independent state sets (537 MB,
     larger than the 256 MB Infinity Cache), so the state cannot stay cached;
-  * prefill: chunked prefill tokens/s at B=1, T=4096 (when built);
+  * prefill: chunked prefill tokens/s at B=1, T=4096;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -61,60 +63,81 @@ def read_traffic(summary_name, source_hash):
 
 
 def decode_bench(args, torch, ops, synth):
+    """The headline: B=64 decode steps, each one gdn_decode_layer launch (conv +
+    L2 norm + gates + recurrence + gated norm), with the conv state alternating
+    between two buffers; then the same step as gdn_conv_update + gdn_decode_step
+    (two launches) for comparison, a burst of back-to-back layer launches (the
+    roofline) and a rotating 4-state-set variant beyond the Infinity Cache."""
     dev = torch.device("cuda:0")
     B, Hk, Hv, d = 64, 16, 32, 128
     QK = Hk * d
+    QKV = 2 * QK + Hv * d
     sets = []
     nsets = 4
     for i in range(nsets):
         W = synth.decode_batch(seed=2 + 1000 * i, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d,
                                head_map=synth.TILED)
         S = {k: (v.to(dev).contiguous() if hasattr(v, "to") else v) for k, v in W.items()}
-        S["y"] = torch.empty((B, 2 * QK + Hv * d), dtype=torch.float32, device=dev)
+        S["conv_b"] = torch.empty_like(S["conv_state"])
+        S["y"] = torch.empty((B, QKV), dtype=torch.float32, device=dev)
         S["out"] = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
+        kw = dict(Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
+                  decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"])
+        x = S["x"]
+        # layer[j]: conv state read from buffer j, written to the other one
+        S["layer"] = [ops.prepare_decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
+                                               S["state"], S["conv_w"], cin, cout, S["out"], **kw)
+                      for cin, cout in ((S["conv_state"], S["conv_b"]),
+                                        (S["conv_b"], S["conv_state"]))]
+        S["parity"] = 0
         S["conv"] = ops.prepare_conv_update(S["x"], S["conv_w"], S["conv_state"], S["y"])
         y = S["y"]
-        S["dec"] = ops.prepare_decode_step(
-            y[:, :QK], y[:, QK:2 * QK], y[:, 2 * QK:], S["state"], S["out"], Hk=Hk, Hv=Hv,
-            dk=d, dv=d, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
-            decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"])
+        S["dec"] = ops.prepare_decode_step(y[:, :QK], y[:, QK:2 * QK], y[:, 2 * QK:], S["state"],
+                                           S["out"], **kw)
         sets.append(S)
     main = sets[0]
 
     def step(S):
-        S["conv"].launch()
-        S["dec"].launch()
+        S["layer"][S["parity"]].launch()
+        S["parity"] ^= 1
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, time.perf_counter() - w0
 
     for _ in range(args.warmup):
         step(main)
     K = args.steps
     # timed region 1 (the metric): K whole steps, one event pair around them
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t0.record()
-    for i in range(K):
-        step(main)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = t0.elapsed_time(t1) / K
-    # timed region 2 (the roofline): K decode launches back to back on the same
-    # stream, one event pair around them -> the decode kernel's average duration
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d0.record()
-    for i in range(K):
+    ms_step, wall = timed(lambda i: step(main), K)
+    # timed region 2 (the roofline): K more layer launches back to back on the same
+    # stream -> the layer kernel's average duration
+    dec_ms, _ = timed(lambda i: step(main), K)
+    # the same step in two launches (conv update, then the decode step)
+    if main["parity"]:  # the two-launch path keeps the window in conv_state
+        main["conv_state"].copy_(main["conv_b"])
+        main["parity"] = 0
+
+    def two(i):
+        main["conv"].launch()
         main["dec"].launch()
-    d1.record()
-    torch.cuda.synchronize()
-    dec_ms = d0.elapsed_time(d1) / K
+    for _ in range(args.warmup):
+        two(0)
+    ms_two, _ = timed(two, K)
 
     state_bytes = 2 * B * Hv * d * d * 4
-    # decode kernel algorithmic bytes: state r+w, q/k/v read (f32 conv output),
-    # z read (bf16), a/b read (bf16), output write (bf16), per-head params
-    act_bytes = B * (2 * QK + Hv * d) * 4 + B * Hv * d * 2 + 2 * B * Hv * 2 + B * Hv * d * 2 \
-        + Hv * 4 * 2 + d * 4
+    # layer kernel algorithmic bytes: state r+w; bf16 x read (q/k/v before the
+    # conv), conv window read and written, conv taps; z, a, b in; bf16 out;
+    # per-head parameters
+    act_bytes = B * QKV * 2 + 2 * B * QKV * 3 * 2 + QKV * 4 * 2 + B * Hv * d * 2 \
+        + 2 * B * Hv * 2 + B * Hv * d * 2 + Hv * 4 * 2 + d * 4
     dec_bytes = state_bytes + act_bytes
     value = state_bytes / (ms_step * 1e-3) / 1e9
 
@@ -123,24 +146,20 @@ def decode_bench(args, torch, ops, synth):
         for S in sets:
             step(S)
     Kr = max(nsets, (K // nsets) * nsets)
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    r0.record()
-    for i in range(Kr):
-        step(sets[i % nsets])
-    r1.record()
-    torch.cuda.synchronize()
-    ms_rot = r0.elapsed_time(r1) / Kr
+    ms_rot, _ = timed(lambda i: step(sets[i % nsets]), Kr)
 
     src_hash = kernel_source_hash(["gdn_decode.hip", "gdn_device.h", "gdn_kernels.h"])
-    traffic = read_traffic("decode_b64_bf16_traffic.md", src_hash)
+    traffic = read_traffic("decode_layer_b64_bf16_traffic.md", src_hash)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
     res = dict(
         value=value, ms_per_step=ms_step, wall_s=wall,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
-                      kernel="gdn decode_kernel<dk=128,dv=128,waves=8,bf16>", bytes_per_launch=dec_bytes,
+                      kernel="gdn decode_kernel<dk=128,dv=128,waves=8,bf16,conv K=4> "
+                             "(gdn_decode_layer)", bytes_per_launch=dec_bytes,
                       avg_launch_us=dec_ms * 1e3, kernel_source_sha256_16=src_hash),
+        two_launch=dict(step="gdn_conv_update + gdn_decode_step", ms_per_step=ms_two,
+                        value=state_bytes / (ms_two * 1e-3) / 1e9, unit="GB/s"),
         rotating=dict(sets=nsets, footprint_mb=nsets * (state_bytes // 2) / 1e6,
                       ms_per_step=ms_rot,
                       value=state_bytes / (ms_rot * 1e-3) / 1e9, unit="GB/s"),
@@ -148,7 +167,8 @@ def decode_bench(args, torch, ops, synth):
                              "bf16 N(0,1) activations, fp32 state N(0,0.02^2), conv K=4",
                     batch=B, tokens_per_seq=1, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map="tiled",
                     act_dtype="bf16", state_dtype="f32", out_dtype="bf16",
-                    step="gdn_conv_update + gdn_decode_step"),
+                    step="gdn_decode_layer (conv + norm + gates + recurrence + gated norm, "
+                         "one launch)"),
     )
     return res
 
@@ -206,9 +226,10 @@ def prefill_bench(torch, ops, synth, calls=20, warmup=5):
 
 
 def counter_pass(torch, ops, synth, steps=10, copy_mib=256):
-    """For HBM-byte counters: `steps` decode steps of the headline workload, then
-    `steps` copies of copy_mib MiB (read and written once each: 2 * copy_mib MiB
-    of traffic per dispatch), whose counter readings calibrate the decode's."""
+    """For HBM-byte counters: `steps` steps of each decode leg of the headline
+    workload (fused layer, two-launch step), then `steps` copies of copy_mib MiB
+    (read and written once each: 2 * copy_mib MiB of traffic per dispatch), whose
+    counter readings calibrate the decode kernels'."""
     args = argparse.Namespace(warmup=2, steps=steps)
     decode_bench(args, torch, ops, synth)
     n = copy_mib * 2 ** 20 // 4
