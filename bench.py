@@ -20,7 +20,11 @@ throughput probe. Also reported on the same JSON line:
   * two_launch: the same step as gdn_conv_update then gdn_decode_step;
   * rotating: the step cycling through 4 independent state sets (537 MB,
     larger than the 256 MB Infinity Cache), so the state cannot stay cached;
-  * prefill: chunked prefill tokens/s at B=1, T=4096;
+  * verify: multi-token verify decode (T = 2, 4, 8 tokens per call) at B=64;
+  * deep_model: 48 layers per token at Hv=48, B=1 and B=32, uncaptured and as
+    one HIP graph;
+  * prefill: chunked prefill tokens/s at B=1, T=4096; prefill_varlen: 8 packed
+    sequences of 512..8192 tokens;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -38,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+VARLEN_LENGTHS = (512, 1024, 2048, 3072, 4096, 5120, 6144, 8192)
 METRIC = "decode state GB/s (% HBM peak); prefill tokens/s at Hv=32,d=128"
 
 
@@ -173,24 +178,147 @@ def decode_bench(args, torch, ops, synth):
     return res
 
 
-def prefill_bench(torch, ops, synth, calls=20, warmup=5):
-    """Chunked prefill, B=1, T=4096, Hk=16, Hv=32, d=128, grouped map, bf16 N(0,1)
-    inputs, raw gates with A_log ~ U[-2,0], q/k L2-normalised in-op, zero initial
-    state, f32 core output (no gated norm)."""
+def verify_bench(torch, ops, synth, Ts=(2, 4, 8), calls=200, warmup=20):
+    """Multi-token verify decode at B=64 (the headline shapes): one gdn_decode_layer
+    call carries T tokens per sequence through the state, which is read and written
+    once per call."""
     dev = torch.device("cuda:0")
-    T, Hk, Hv, d = 4096, 16, 32, 128
-    P = synth.prefill(seed=3, lengths=[T], Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.GROUPED)
+    B, Hk, Hv, d = 64, 16, 32, 128
+    QK = Hk * d
+    res = {}
+    for T in Ts:
+        W = synth.decode_batch(seed=20 + T, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d, T=T,
+                               head_map=synth.TILED)
+        S = {k: (v.to(dev).contiguous() if hasattr(v, "to") else v) for k, v in W.items()}
+        cb = torch.empty_like(S["conv_state"])
+        out = torch.empty((B * T, Hv, d), dtype=torch.bfloat16, device=dev)
+        x = S["x"]
+        calls_ = [ops.prepare_decode_layer(
+            x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:], S["state"], S["conv_w"], ci, co, out,
+            Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=B, tokens_per_seq=T, a=S["a"],
+            b=S["b"], decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"],
+            norm_weight=S["norm_w"]) for ci, co in ((S["conv_state"], cb), (cb, S["conv_state"]))]
+        for i in range(warmup):
+            calls_[i & 1].launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(calls):
+            calls_[i & 1].launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        state_bytes = 2 * B * Hv * d * d * 4
+        res[f"T{T}"] = dict(ms_per_call=ms, tokens_per_s=B * T / (ms * 1e-3),
+                            state_GBps=state_bytes / (ms * 1e-3) / 1e9,
+                            state_GBps_per_token=state_bytes * T / (ms * 1e-3) / 1e9)
+    return dict(workload="multi-token verify decode: B=64 x T tokens per call, Hk=16, Hv=32, "
+                         "dk=dv=128, tiled map, bf16 N(0,1), one gdn_decode_layer call",
+                **res)
+
+
+def deep_model_bench(torch, ops, synth, batches=(1, 32), layers=48, steps=(100, 20)):
+    """Deep-model decode: Hk=16, Hv=48, d=128, `layers` layers applied in sequence per
+    token, each with its own seeded taps, gates, norm, state and conv window (seed
+    4*1000 + layer); one token step = `layers` gdn_decode_layer launches. Timed
+    uncaptured and as one captured HIP graph (two token steps per graph, so the conv
+    windows alternate back to their first buffers)."""
+    dev = torch.device("cuda:0")
+    Hk, Hv, d = 16, 48, 128
+    QK = Hk * d
+    res = {}
+    for B, nsteps in zip(batches, steps):
+        cap = torch.cuda.Stream()
+        Ls = []
+        for layer in range(layers):
+            W = synth.decode_batch(seed=4 * 1000 + layer, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d,
+                                   head_map=synth.TILED)
+            S = {k: (v.to(dev).contiguous() if hasattr(v, "to") else v) for k, v in W.items()}
+            S["cb"] = torch.empty_like(S["conv_state"])
+            S["out"] = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
+            x = S["x"]
+            kw = dict(Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=B, a=S["a"],
+                      b=S["b"], decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"],
+                      norm_weight=S["norm_w"])
+            pairs = ((S["conv_state"], S["cb"]), (S["cb"], S["conv_state"]))
+            S["eager"] = [ops.prepare_decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
+                                                   S["state"], S["conv_w"], ci, co, S["out"],
+                                                   **kw) for ci, co in pairs]
+            S["cap"] = [ops.prepare_decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
+                                                 S["state"], S["conv_w"], ci, co, S["out"],
+                                                 stream=cap, **kw) for ci, co in pairs]
+            Ls.append(S)
+
+        def token(par, key):
+            for S in Ls:
+                S[key][par].launch()
+
+        for i in range(4):
+            token(i & 1, "eager")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(nsteps):
+            token(i & 1, "eager")
+        e1.record()
+        torch.cuda.synchronize()
+        ms_eager = e0.elapsed_time(e1) / nsteps
+        if nsteps % 2:
+            token(1, "eager")  # back to parity 0
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            token(0, "cap")
+            token(1, "cap")
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, nsteps // 2)
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / (2 * reps)
+        state_bytes = 2 * layers * B * Hv * d * d * 4
+        res[f"B{B}"] = dict(ms_per_token_step=ms_eager, ms_per_token_step_graph=ms_graph,
+                            state_GBps=state_bytes / (ms_eager * 1e-3) / 1e9,
+                            state_GBps_graph=state_bytes / (ms_graph * 1e-3) / 1e9,
+                            state_bytes_per_step=state_bytes)
+        del graph, Ls
+        torch.cuda.empty_cache()
+    return dict(workload=f"deep-model decode: {layers} layers x gdn_decode_layer per token, "
+                         "Hk=16, Hv=48, dk=dv=128, tiled map, bf16 N(0,1), fp32 states",
+                **res)
+
+
+def prefill_bench(torch, ops, synth, *, lengths=(4096,), head_map=None, state_std=0.0,
+                  out_dtype=None, seed=3, calls=20, warmup=5, workload=None):
+    """Chunked prefill over packed sequences of the given lengths, Hk=16, Hv=32,
+    d=128, bf16 N(0,1) inputs, raw gates with A_log ~ U[-2,0], q/k L2-normalised
+    in-op, initial states N(0, state_std^2), core output (no gated norm). Defaults:
+    config 3 (one sequence of 4096 tokens, grouped map, zero state, f32 out)."""
+    dev = torch.device("cuda:0")
+    Hk, Hv, d = 16, 32, 128
+    head_map = synth.GROUPED if head_map is None else head_map
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    P = synth.prefill(seed=seed, lengths=list(lengths), Hk=Hk, Hv=Hv, dk=d, dv=d,
+                      head_map=head_map, state_std=state_std)
+    T = int(P["cu_seqlens"][-1])
+    N = len(lengths)
     g = lambda t: t.reshape(T, -1).to(dev).contiguous()  # noqa: E731
     q, k, v, a, b = g(P["q"]), g(P["k"]), g(P["v"]), g(P["a"]), g(P["b"])
     state0 = P["state"].to(dev).contiguous()
     state = state0.clone()
-    out = torch.empty((T, Hv, d), dtype=torch.float32, device=dev)
+    out = torch.empty((T, Hv, d), dtype=out_dtype, device=dev)
     cu_h = P["cu_seqlens"].contiguous()
     cu_d = cu_h.to(dev)
-    need = ops.prefill_workspace_bytes(Hk=Hk, Hv=Hv, dk=d, dv=d, num_seqs=1, total_tokens=T)
+    need = ops.prefill_workspace_bytes(Hk=Hk, Hv=Hv, dk=d, dv=d, num_seqs=N, total_tokens=T)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     call = ops.prepare_prefill_chunked(q, k, v, state, cu_d, cu_h, out, ws, Hk=Hk, Hv=Hv, dk=d,
-                                       dv=d, head_map=synth.GROUPED, a=a, b=b,
+                                       dv=d, head_map=head_map, a=a, b=b,
                                        decay_param=P["A_log"].to(dev),
                                        dt_bias=P["dt_bias"].to(dev))
     for _ in range(warmup):
@@ -198,7 +326,7 @@ def prefill_bench(torch, ops, synth, calls=20, warmup=5):
         call.launch()
     times = []
     for _ in range(calls):
-        state.copy_(state0)  # every call starts from the zero state (outside the timed span)
+        state.copy_(state0)  # every call starts from the same state (outside the timed span)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         call.launch()
@@ -208,17 +336,16 @@ def prefill_bench(torch, ops, synth, calls=20, warmup=5):
     times.sort()
     ms = times[len(times) // 2]
     C = 64
-    chunks = T // C
+    chunks = sum((n + C - 1) // C for n in lengths)
     # algorithmic MFMA work of the chunked form, per (chunk, v-head): U, W (2 C^2 d
     # each), W S^T, Q S^T, D^T K (2 C d^2 each), Aqk D (2 C^2 d); per (chunk, k-head):
     # K K^T and Q K^T (2 C^2 d each)
     flops = chunks * (Hv * (3 * 2 * C * C * d + 3 * 2 * C * d * d) + Hk * 2 * 2 * C * C * d)
-    # HBM bytes: bf16 q, k, v, a, b in; f32 output; the state read and written once
-    hbm = T * (2 * Hk * d + Hv * d + 2 * Hv) * 2 + T * Hv * d * 4 + 2 * Hv * d * d * 4
+    # HBM bytes: bf16 q, k, v, a, b in; the output; the states read and written once
+    osz = 4 if out_dtype == torch.float32 else 2
+    hbm = T * (2 * Hk * d + Hv * d + 2 * Hv) * 2 + T * Hv * d * osz + 2 * N * Hv * d * d * 4
     t = ms * 1e-3
-    return dict(workload="chunked prefill: B=1, T=4096, C=64, Hk=16, Hv=32, dk=dv=128, grouped "
-                         "map, bf16 N(0,1) inputs, q/k L2-normalised, raw gates, zero initial "
-                         "state, f32 core output",
+    return dict(workload=workload, tokens=T, sequences=N, chunks=chunks,
                 tokens_per_s=T / t, ms_per_call=ms, calls=calls, unit="tokens/s",
                 mfma_flops=flops, mfma_util=flops / t / (MFMA_F16_PEAK_TFLOPS * 1e12),
                 roofline=dict(bound="hbm", achieved=hbm / t / 1e9, peak=HBM_PEAK_GBS,
@@ -280,6 +407,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the multi-token and the 48-layer decode legs")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: a few decode steps, then a plain "
                          "256 MiB device copy of known size (the counters' calibration)")
@@ -313,12 +442,31 @@ def main():
                 data="synthetic", config=dec["config"],
                 pct_hbm_peak=round(100 * dec["value"] / HBM_PEAK_GBS, 2),
                 roofline=dec["roofline"], rotating=dec["rotating"])
+    if not args.no_verify:
+        print("[bench] multi-token verify decode, T=2,4,8", file=sys.stderr, flush=True)
+        line["verify"] = verify_bench(torch, ops, synth)
+        print("[bench] deep-model decode, 48 layers, B=1 and B=32", file=sys.stderr, flush=True)
+        line["deep_model"] = deep_model_bench(torch, ops, synth)
     if not args.no_prefill:
         print("[bench] prefill T=4096", file=sys.stderr, flush=True)
-        pre = prefill_bench(torch, ops, synth)
+        pre = prefill_bench(
+            torch, ops, synth,
+            workload="chunked prefill: B=1, T=4096, C=64, Hk=16, Hv=32, dk=dv=128, grouped map, "
+                     "bf16 N(0,1) inputs, q/k L2-normalised, raw gates, zero initial state, "
+                     "f32 core output")
         print(f"[bench] prefill {pre['tokens_per_s'] / 1e6:.2f} M tokens/s, "
               f"{pre['ms_per_call'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
         line["prefill"] = pre
+        print("[bench] varlen prefill, 8 sequences", file=sys.stderr, flush=True)
+        var = prefill_bench(
+            torch, ops, synth, lengths=VARLEN_LENGTHS, head_map=synth.TILED, state_std=0.02,
+            out_dtype=torch.bfloat16, seed=5,
+            workload="varlen chunked prefill: 8 sequences of 512..8192 tokens (30,208 packed), "
+                     "C=64, Hk=16, Hv=32, dk=dv=128, tiled map, bf16 N(0,1) inputs, raw gates, "
+                     "initial states N(0,0.02^2), bf16 core output")
+        print(f"[bench] varlen prefill {var['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+              f"{var['ms_per_call'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+        line["prefill_varlen"] = var
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
