@@ -20,19 +20,19 @@
 // Kernels:
 //  1. plan_kernel   -- chunk table: 64-token chunks from each sequence's first
 //                      token (the last may be short; none straddles sequences).
-//  2. prep_kernel   -- per (chunk, v-head), all chunks in parallel: q/k L2 norm,
-//                      gates and their in-chunk prefix sums, the gram K K^T and
-//                      Q K^T (f16 MFMA), T = (I + A)^-1 in f32 (16x16 diagonal
-//                      blocks by substitution, off-diagonal blocks by f32 MFMA
-//                      block products), then U and W (f16 MFMA). Writes U (f32),
-//                      W, Aqk, the normalised Q and K^T (f16) and G to the workspace.
+//  2. prep_kernel   -- per (chunk, k-head), all chunks in parallel: q/k L2 norm,
+//                      the gram K K^T and Q K^T (f16 MFMA, Q K^T from hi + lo
+//                      parts), the normalised Q and K^T for the workspace; then for
+//                      each v-head reading that k-head: gates and their in-chunk
+//                      prefix sums, T = (I + A)^-1 in f32 (16x16 diagonal blocks by
+//                      substitution, off-diagonal blocks by f32 MFMA block
+//                      products), U and W (f16 MFMA), Aqk and the decay rows.
 //  3. carry_kernel  -- per (sequence, v-head, 16-row slice of dv), sequential
-//                      over the sequence's chunks: the state slice stays in MFMA
-//                      accumulators (f32) with an f16 copy in LDS as an operand;
-//                      D, O and the next state per chunk on f16 MFMA with f32
-//                      accumulation. D enters the state update as an f16 hi+lo
-//                      pair. The next chunk's operands are prefetched into VGPRs
-//                      while the current chunk is computed.
+//                      over the sequence's chunks, one wave per slice: the slice's
+//                      S^T stays in MFMA accumulators (f32), rounded to f16 as the
+//                      B operand of W S^T and Q S^T; D enters the state update and
+//                      the output as f16 hi + lo pairs. Each chunk's operands are
+//                      copied global -> LDS one chunk ahead.
 //  4. norm_kernel   -- gated RMS norm of the f32 core output (optional).
 
 #include "gdn_device.h"
@@ -156,16 +156,21 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
 
 // ---------------------------------------------------------------- 2. prep
 
+// One workgroup per (chunk, k-head): the normalised q/k rows, K K^T, Q K^T and
+// the workspace's Q and K^T are formed once and serve the Hv/Hk v-heads that
+// read this k-head, which the workgroup then takes in turn (gates, A and Aqk,
+// the inverse, U and W, the decay rows).
 template <int QT>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 {
-    // LDS: X1 = normalised K rows (f16) then A / T (f32, in place);
-    //      X2 = normalised Q rows (f16), the block-product scratch (f32), then W (f16).
+    // LDS: X1 = normalised K rows (f16) then A / T (f32, in place, per v-head);
+    //      X2 = normalised Q rows (f16), then per v-head the block-product
+    //      scratch (f32) and W (f16, staged for the store).
     // K and Q rows are stored with dk in the permuted order, which W and Q keep.
     __shared__ __attribute__((aligned(16))) unsigned char X1[C * AP * 4];
     __shared__ __attribute__((aligned(16))) unsigned char X2[C * KP * 2];
-    __shared__ __attribute__((aligned(16))) _Float16 VbT[DH][TP];  // beta_t v_t, [dv][token slot]
-    __shared__ __attribute__((aligned(16))) _Float16 KbT[DH][TP];  // beta_t gamma_t k_t, [dk slot][token slot]
+    __shared__ __attribute__((aligned(16))) _Float16 VT[DH][TP];  // v, [dv][token slot] (per v-head)
+    __shared__ __attribute__((aligned(16))) _Float16 KT[DH][TP];  // k, [dk slot][token slot]
     __shared__ float G_s[C], beta_s[C], bg_s[C];
     static_assert(C * AP * 4 >= C * KP * 2, "X1 holds both the K rows and A / T");
     static_assert(C * KP * 2 >= 32 * 36 * 4, "X2 holds the Q rows and the 32x32 scratch");
@@ -174,52 +179,34 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     _Float16(*Qh)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);
     // f16 remainders (x - f16(x)) of the normalised rows, for Q K^T; they live
     // in the transposed tiles' space, which is filled only after that product
-    _Float16(*Kl)[KP] = reinterpret_cast<_Float16(*)[KP]>(&VbT[0][0]);
-    _Float16(*Ql)[KP] = reinterpret_cast<_Float16(*)[KP]>(&KbT[0][0]);
-    static_assert(sizeof(VbT) >= C * KP * 2, "VbT holds the K remainders");
+    _Float16(*Kl)[KP] = reinterpret_cast<_Float16(*)[KP]>(&VT[0][0]);
+    _Float16(*Ql)[KP] = reinterpret_cast<_Float16(*)[KP]>(&KT[0][0]);
+    static_assert(sizeof(VT) >= C * KP * 2, "VT holds the K remainders");
     float(*Am)[AP] = reinterpret_cast<float(*)[AP]>(X1);
     float(*Pm)[36] = reinterpret_cast<float(*)[36]>(X2);
 
     const HeadCfg &hc = p.hc;
     const ActInputs &in = p.in;
-    const int Hv = hc.Hv, Hk = hc.Hk;
-    const int chunk = blockIdx.x / Hv;
-    const int h = blockIdx.x % Hv;
-    const int kh = k_head_of(hc.head_map, h, Hk, Hv);
+    const int Hv = hc.Hv, Hk = hc.Hk, G = Hv / Hk;
+    const int chunk = blockIdx.x / Hk;
+    const int kh = blockIdx.x % Hk;
     const int tok0 = p.chunk_start[chunk];
     const int n = p.chunk_len[chunk];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
     const uint32_t flags = hc.flags;
-    // one of the v-heads reading kh writes the normalised Q and K^T for the carry
-    const bool qk_writer = hc.head_map == 0 ? (h % (Hv / Hk) == 0) : (h < Hk);
-
-    // -- gates and their prefix sums (wave 0, lane = token)
-    if (wave == 0) {
-        float g = 0.f, beta = 0.f;
-        if (lane < n) {
-            const int64_t gi = (int64_t)(tok0 + lane) * Hv + h;
-            if (flags & F_RAW_GATES) {
-                const float dp = in.decay_param[h];
-                const float rate = hc.decay_kind == 0 ? -expf(dp) : dp;
-                g = rate * softplus_f(load_act(in.a, gi, in.ab_dt) + in.dt_bias[h]);
-                beta = sigmoid_f(load_act(in.b, gi, in.ab_dt));
-            } else {
-                g = in.g[gi];
-                beta = in.beta[gi];
-            }
-        }
-        float G = g;
+    // the j-th v-head reading kh (the inverse of the head map)
+    auto vhead = [&](int j) { return hc.head_map == 0 ? kh * G + j : kh + j * Hk; };
+    // transposed tiles: thread = (four adjacent dims dq, token octet oc), the
+    // octet being token slots 8 oc .. 8 oc + 7 of the permuted order
+    const int dq = threadIdx.x & 31, oc = threadIdx.x >> 5;
+    auto load_v = [&](Raw4<QT> (&vr)[8], int h) {
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(G, off, 64);
-            if (lane >= off)
-                G += o;
+        for (int i = 0; i < 8; ++i) {
+            const int t = perm_idx(8 * oc + i);
+            vr[i] = load_raw4<QT>(in.v, (int64_t)(tok0 + min(t, n - 1)) * in.v_stride + (int64_t)h * DH + 4 * dq);
         }
-        G_s[lane] = G;  // tokens >= n carry G_{n-1} (their g is 0)
-        beta_s[lane] = beta;
-        bg_s[lane] = beta * __expf(G);
-    }
-    __syncthreads();
+    };
 
     // -- rows of k and q: wave w loads tokens 16w .. 16w+15, 32 lanes per row;
     // rows past the chunk's end re-read its last row and are zeroed after.
@@ -262,19 +249,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     }
     __syncthreads();
 
-    // Transposed tiles are built after the products below by thread = (four
-    // adjacent dims dq, token octet o), the octet being token slots 8o .. 8o+7 of
-    // the permuted order; its v rows are loaded now so the products hide them.
-    const int dq = threadIdx.x & 31, oc = threadIdx.x >> 5;
+    // the first v-head's v rows, in flight during the products below
     Raw4<QT> vr[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = perm_idx(8 * oc + i);
-        vr[i] = load_raw4<QT>(in.v, (int64_t)(tok0 + min(t, n - 1)) * in.v_stride + (int64_t)h * DH + 4 * dq);
-    }
+    load_v(vr, vhead(0));
 
     // -- K K^T and Q K^T on the lower block triangle: wave w owns token rows 16w..
-    const int li = lane & 15, lg = lane >> 4;
     f32x4 gram[4], qk[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -299,44 +278,28 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
 
     __syncthreads();  // the remainders are dead: the transposed tiles take their space
 
-    // -- transposed tiles: beta v (dims natural) and beta gamma k (dims in slot
-    // order) as [dim][token slot]; the K^T the carry reads ([dk][token slot], dk
+    // -- K as [dk slot][token slot]; the K^T the carry reads ([dk][token slot], dk
     // natural) goes straight to the workspace from the same registers
     {
         typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-        half8 vb[4], kb[4], kt[4];
+        half8 kt[4];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int t = perm_idx(8 * oc + i);
-            const float4 vf = raw4_to_f32<QT>(vr[i]);
-            const float bt = beta_s[t], bgt = bg_s[t];  // 0 for tokens past the chunk's end
-            const half4 kq = *reinterpret_cast<const half4 *>(&Kh[t][4 * dq]);
-            vb[0][i] = (_Float16)(bt * vf.x);
-            vb[1][i] = (_Float16)(bt * vf.y);
-            vb[2][i] = (_Float16)(bt * vf.z);
-            vb[3][i] = (_Float16)(bt * vf.w);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                kb[d][i] = (_Float16)(bgt * (float)kq[d]);
-                kt[d][i] = kq[d];
-            }
-        }
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            *reinterpret_cast<half8 *>(&VbT[4 * dq + d][8 * oc]) = vb[d];
-            *reinterpret_cast<half8 *>(&KbT[4 * dq + d][8 * oc]) = kb[d];
-        }
-        if (qk_writer) {
-            uint16_t *kdst = p.knT + ((int64_t)chunk * Hk + kh) * DH * C;
-            const int dk0 = perm_idx(4 * dq);  // slots 4dq .. 4dq+3 hold dk0 .. dk0+3
+            const half4 kq = *reinterpret_cast<const half4 *>(&Kh[perm_idx(8 * oc + i)][4 * dq]);
 #pragma unroll
             for (int d = 0; d < 4; ++d)
-                *reinterpret_cast<half8 *>(kdst + (dk0 + d) * C + 8 * oc) = kt[d];
+                kt[d][i] = kq[d];
+        }
+        uint16_t *kdst = p.knT + ((int64_t)chunk * Hk + kh) * DH * C;
+        const int dk0 = perm_idx(4 * dq);  // slots 4dq .. 4dq+3 hold dk0 .. dk0+3
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            *reinterpret_cast<half8 *>(&KT[4 * dq + d][8 * oc]) = kt[d];
+            *reinterpret_cast<half8 *>(kdst + (dk0 + d) * C + 8 * oc) = kt[d];
         }
     }
-
     // normalised Q rows (dk already in slot order) go to the workspace
-    if (qk_writer) {
+    {
         uint16_t *qdst = p.qn + ((int64_t)chunk * Hk + kh) * C * DH;
 #pragma unroll
         for (int k = 0; k < (C * DH / 8) / 256; ++k) {
@@ -345,135 +308,189 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             *reinterpret_cast<half8 *>(qdst + t * DH + c8) = lds_half8(&Qh[t][c8]);
         }
     }
-    __syncthreads();  // Kh / Qh are dead from here: X1 becomes A / T, X2 scratch
 
-    // -- A (strictly lower, f32) into X1; decayed, masked Q K^T to the workspace
-    {
-        uint16_t *aq = p.aqk + ((int64_t)chunk * Hv + h) * C * C;
+    for (int j = 0; j < G; ++j) {
+        const int h = vhead(j);
+        // the previous v-head is done with LDS (W copied out, tiles read)
+        __syncthreads();
+        // -- gates and their prefix sums (wave 0, lane = token)
+        if (wave == 0) {
+            float g = 0.f, beta = 0.f;
+            if (lane < n) {
+                const int64_t gi = (int64_t)(tok0 + lane) * Hv + h;
+                if (flags & F_RAW_GATES) {
+                    const float dp = in.decay_param[h];
+                    const float rate = hc.decay_kind == 0 ? -expf(dp) : dp;
+                    g = rate * softplus_f(load_act(in.a, gi, in.ab_dt) + in.dt_bias[h]);
+                    beta = sigmoid_f(load_act(in.b, gi, in.ab_dt));
+                } else {
+                    g = in.g[gi];
+                    beta = in.beta[gi];
+                }
+            }
+            float Gc = g;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(Gc, off, 64);
+                if (lane >= off)
+                    Gc += o;
+            }
+            G_s[lane] = Gc;  // tokens >= n carry G_{n-1} (their g is 0)
+            beta_s[lane] = beta;
+            bg_s[lane] = beta * __expf(Gc);
+        }
+        // -- v as [dv][token slot]
+        {
+            half8 vb[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = wave * 16 + lg * 4 + r, s = j * 16 + li;
-                const float dg = s <= t ? __expf(G_s[t] - G_s[s]) : 0.f;
-                Am[t][s] = s < t ? beta_s[t] * dg * gram[j][r] : 0.f;
-                aq[t * C + perm_pos(s)] = f32_to_f16_bits(-hc.scale * dg * qk[j][r]);
+            for (int i = 0; i < 8; ++i) {
+                const float4 vf = raw4_to_f32<QT>(vr[i]);
+                vb[0][i] = (_Float16)vf.x;
+                vb[1][i] = (_Float16)vf.y;
+                vb[2][i] = (_Float16)vf.z;
+                vb[3][i] = (_Float16)vf.w;
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                *reinterpret_cast<half8 *>(&VT[4 * dq + d][8 * oc]) = vb[d];
+        }
+        if (j + 1 < G)
+            load_v(vr, vhead(j + 1));  // the next v-head's rows, in flight from here
+        __syncthreads();
+
+        // -- A (strictly lower, f32) into X1; decayed, masked, scaled -Q K^T to the workspace
+        {
+            uint16_t *aq = p.aqk + ((int64_t)chunk * Hv + h) * C * C;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = wave * 16 + lg * 4 + r, s = jj * 16 + li;
+                    const float dg = s <= t ? __expf(G_s[t] - G_s[s]) : 0.f;
+                    Am[t][s] = s < t ? beta_s[t] * dg * gram[jj][r] : 0.f;
+                    aq[t * C + perm_pos(s)] = f32_to_f16_bits(-hc.scale * dg * qk[jj][r]);
+                }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // -- T = (I + A)^-1 in place. (a) the four 16x16 diagonal blocks by forward
-    // substitution: wave 0, lane = (block, column).
-    if (wave == 0) {
-        const int b0 = (lane >> 4) * 16, c = lane & 15;
-        float x[16];
+        // -- T = (I + A)^-1 in place. (a) the four 16x16 diagonal blocks by forward
+        // substitution: wave 0, lane = (block, column).
+        if (wave == 0) {
+            const int b0 = (lane >> 4) * 16, c = lane & 15;
+            float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float acc = 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s)
-                acc += Am[b0 + r][b0 + s] * x[s];
-            x[r] = r < c ? 0.f : (r == c ? 1.f : -acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            Am[b0 + r][b0 + c] = x[r];
-    }
-    __syncthreads();
-    // (b) 32x32 diagonal halves: T10 = -T11 (A10 T00), waves 0 and 1 (blocks 1,0 and 3,2)
-    if (wave < 2) {
-        const int bi = (2 * wave + 1) * 16, bj = 2 * wave * 16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            acc = mfma4(Am[bi + li][bj + ks * 4 + lg], Am[bj + ks * 4 + lg][bj + li], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Pm[wave * 16 + lg * 4 + r][li] = acc[r];
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const int bi = (2 * wave + 1) * 16, bj = 2 * wave * 16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            acc = mfma4(Am[bi + li][bi + ks * 4 + lg], Pm[wave * 16 + ks * 4 + lg][li], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Am[bi + lg * 4 + r][bj + li] = -acc[r];
-    }
-    __syncthreads();
-    // (c) lower-left 32x32: T_LL = -T_11 (A_LL T_00); wave = one 16x16 output tile
-    {
-        const int ti = wave >> 1, tj = wave & 1;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            acc = mfma4(Am[32 + ti * 16 + li][ks * 4 + lg], Am[ks * 4 + lg][tj * 16 + li], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Pm[ti * 16 + lg * 4 + r][tj * 16 + li] = acc[r];
-    }
-    __syncthreads();
-    {
-        const int ti = wave >> 1, tj = wave & 1;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            acc = mfma4(Am[32 + ti * 16 + li][32 + ks * 4 + lg], Pm[ks * 4 + lg][tj * 16 + li], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Am[32 + ti * 16 + lg * 4 + r][tj * 16 + li] = -acc[r];
-    }
-    __syncthreads();
-
-    // -- U = T (beta V) and W = T (beta gamma K): wave w owns token rows 16w..;
-    // the contraction runs over token slots, so T's columns are taken in slot order
-    {
-        half8 ta[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                ta[ks][i] = (_Float16)Am[wave * 16 + li][perm_idx(ks * 32 + lg * 8 + i)];
-        float *ud = p.umat + ((int64_t)chunk * Hv + h) * DH * C;
-        _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);  // W rows, staged
-#pragma unroll
-        for (int nt = 0; nt < DH / 16; ++nt) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                u = mfma16(ta[ks], lds_half8(&VbT[nt * 16 + li][ks * 32 + lg * 8]), u);
-                w = mfma16(ta[ks], lds_half8(&KbT[nt * 16 + li][ks * 32 + lg * 8]), w);
+                for (int s = 0; s < r; ++s)
+                    acc += Am[b0 + r][b0 + s] * x[s];
+                x[r] = r < c ? 0.f : (r == c ? 1.f : -acc);
             }
-            // -U^T: this lane's four tokens are adjacent in row dv
-            *reinterpret_cast<f32x4 *>(ud + (nt * 16 + li) * C + wave * 16 + lg * 4) = -u;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                Am[b0 + r][b0 + c] = x[r];
+        }
+        __syncthreads();
+        // (b) 32x32 diagonal halves: T10 = -T11 (A10 T00), waves 0 and 1 (blocks 1,0 and 3,2)
+        if (wave < 2) {
+            const int bi = (2 * wave + 1) * 16, bj = 2 * wave * 16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mfma4(Am[bi + li][bj + ks * 4 + lg], Am[bj + ks * 4 + lg][bj + li], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Wl[wave * 16 + lg * 4 + r][nt * 16 + li] = (_Float16)w[r];
+                Pm[wave * 16 + lg * 4 + r][li] = acc[r];
         }
-    }
-    if (threadIdx.x < C) {
-        // decay rows the carry multiplies by: gamma_t = exp(G_t),
-        // -exp(G_last - G_t) (negated because the carry holds -D) and
-        // scale gamma_t; G_last = G at the chunk's last token = G_s[C-1]
-        float *gd = p.gcum + ((int64_t)chunk * Hv + h) * 4 * C;
-        const float gm = __expf(G_s[threadIdx.x]);
-        gd[threadIdx.x] = gm;
-        gd[C + threadIdx.x] = -__expf(G_s[C - 1] - G_s[threadIdx.x]);
-        gd[2 * C + threadIdx.x] = hc.scale * gm;
-        gd[3 * C + threadIdx.x] = 0.f;
-    }
-    __syncthreads();
-    {
-        uint16_t *wd = p.wmat + ((int64_t)chunk * Hv + h) * C * DH;
-        _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);
+        __syncthreads();
+        if (wave < 2) {
+            const int bi = (2 * wave + 1) * 16, bj = 2 * wave * 16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < (C * DH / 8) / 256; ++k) {
-            const int e = k * 256 + threadIdx.x;
-            const int t = e / (DH / 8), c8 = (e % (DH / 8)) * 8;
-            *reinterpret_cast<half8 *>(wd + t * DH + c8) = lds_half8(&Wl[t][c8]);
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mfma4(Am[bi + li][bi + ks * 4 + lg], Pm[wave * 16 + ks * 4 + lg][li], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Am[bi + lg * 4 + r][bj + li] = -acc[r];
+        }
+        __syncthreads();
+        // (c) lower-left 32x32: T_LL = -T_11 (A_LL T_00); wave = one 16x16 output tile
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                acc = mfma4(Am[32 + ti * 16 + li][ks * 4 + lg], Am[ks * 4 + lg][tj * 16 + li], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Pm[ti * 16 + lg * 4 + r][tj * 16 + li] = acc[r];
+        }
+        __syncthreads();
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                acc = mfma4(Am[32 + ti * 16 + li][32 + ks * 4 + lg], Pm[ks * 4 + lg][tj * 16 + li], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Am[32 + ti * 16 + lg * 4 + r][tj * 16 + li] = -acc[r];
+        }
+        __syncthreads();
+
+        // -- U = T diag(beta) V and W = T diag(beta gamma) K: wave w owns token rows
+        // 16w..; the contraction runs over token slots, so T's columns are taken in
+        // slot order, each scaled by its token's beta (U) or beta gamma (W)
+        {
+            half8 tu[2], tw[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int s = perm_idx(ks * 32 + lg * 8 + i);
+                    const float tv = Am[wave * 16 + li][s];
+                    tu[ks][i] = (_Float16)(tv * beta_s[s]);
+                    tw[ks][i] = (_Float16)(tv * bg_s[s]);
+                }
+            float *ud = p.umat + ((int64_t)chunk * Hv + h) * DH * C;
+            _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);  // W rows, staged
+#pragma unroll
+            for (int nt = 0; nt < DH / 16; ++nt) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    u = mfma16(tu[ks], lds_half8(&VT[nt * 16 + li][ks * 32 + lg * 8]), u);
+                    w = mfma16(tw[ks], lds_half8(&KT[nt * 16 + li][ks * 32 + lg * 8]), w);
+                }
+                // -U^T: this lane's four tokens are adjacent in row dv
+                *reinterpret_cast<f32x4 *>(ud + (nt * 16 + li) * C + wave * 16 + lg * 4) = -u;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Wl[wave * 16 + lg * 4 + r][nt * 16 + li] = (_Float16)w[r];
+            }
+        }
+        if (threadIdx.x < C) {
+            // decay rows the carry multiplies by: gamma_t = exp(G_t),
+            // -exp(G_last - G_t) (negated because the carry holds -D) and
+            // scale gamma_t; G_last = G at the chunk's last token = G_s[C-1]
+            float *gd = p.gcum + ((int64_t)chunk * Hv + h) * 4 * C;
+            const float gm = __expf(G_s[threadIdx.x]);
+            gd[threadIdx.x] = gm;
+            gd[C + threadIdx.x] = -__expf(G_s[C - 1] - G_s[threadIdx.x]);
+            gd[2 * C + threadIdx.x] = hc.scale * gm;
+            gd[3 * C + threadIdx.x] = 0.f;
+        }
+        __syncthreads();
+        {
+            uint16_t *wd = p.wmat + ((int64_t)chunk * Hv + h) * C * DH;
+            _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);
+#pragma unroll
+            for (int k = 0; k < (C * DH / 8) / 256; ++k) {
+                const int e = k * 256 + threadIdx.x;
+                const int t = e / (DH / 8), c8 = (e % (DH / 8)) * 8;
+                *reinterpret_cast<half8 *>(wd + t * DH + c8) = lds_half8(&Wl[t][c8]);
+            }
         }
     }
 }
@@ -888,7 +905,7 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
     if (p.num_chunks == 0)
         return hipSuccess;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
-    const dim3 pgrid((unsigned)((int64_t)p.num_chunks * p.hc.Hv));
+    const dim3 pgrid((unsigned)((int64_t)p.num_chunks * p.hc.Hk));
     switch (p.in.qkv_dt) {
     case DT_F32: hipLaunchKernelGGL((prep_kernel<DT_F32>), pgrid, dim3(256), 0, s, p); break;
     case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
