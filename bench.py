@@ -441,7 +441,8 @@ def main():
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
                 data="synthetic", config=dec["config"],
                 pct_hbm_peak=round(100 * dec["value"] / HBM_PEAK_GBS, 2),
-                roofline=dec["roofline"], rotating=dec["rotating"])
+                roofline=dec["roofline"], two_launch=dec["two_launch"],
+                rotating=dec["rotating"])
     if not args.no_verify:
         print("[bench] multi-token verify decode, T=2,4,8", file=sys.stderr, flush=True)
         line["verify"] = verify_bench(torch, ops, synth)

@@ -81,6 +81,8 @@ gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dty
             return GDN_ERR_NULL;
         if (!dtype_ok(in->z_dtype))
             return GDN_ERR_UNSUPPORTED;
+        if (!aligned(in->z, 4) || !aligned(in->norm_weight, 4))
+            return GDN_ERR_ALIGN;  // z is read as aligned 32-bit words
     }
     if (!aligned(state, 16))
         return GDN_ERR_ALIGN;

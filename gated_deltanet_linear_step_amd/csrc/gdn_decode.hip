@@ -213,6 +213,33 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         S[i] = load_state4(Sg + (row0 + i * RPI) * DK + col);
+    // the gated norm's z and weights for the first token group, behind the state:
+    // the epilogue then waits on nothing (branch-free: without the norm the loads
+    // read the state's first word and are not used)
+    constexpr int ZT = (kTokGroup + NW - 1) / NW, ZJ = (DV + 63) / 64;
+    const bool gated = flags & F_GATED_NORM;
+    uint32_t zw[ZT][ZJ];
+    float nw[ZJ];
+    auto prefetch_z = [&](int t0, int tn) {
+        const void *zsrc = gated ? p.in.z : static_cast<const void *>(p.state);
+#pragma unroll
+        for (int i = 0; i < ZT; ++i) {
+            const int tt = wave + i * NW;
+            const int64_t obase = (((int64_t)b * p.T + t0 + tt) * Hv + h) * DV;
+#pragma unroll
+            for (int m = 0; m < ZJ; ++m) {
+                const int j = lane + 64 * m;
+                const bool use = gated && tt < tn && j < DV;
+                zw[i][m] = load_word_nb(zsrc, use ? obase + j : 0, p.in.z_dt);
+            }
+        }
+    };
+    prefetch_z(0, min(p.T, kTokGroup));
+#pragma unroll
+    for (int m = 0; m < ZJ; ++m) {
+        const int j = lane + 64 * m;
+        nw[m] = (gated ? p.in.norm_w : p.state)[gated && j < DV ? j : 0];
+    }
     __builtin_amdgcn_sched_barrier(0);  // ... and their use behind the state loads
     const bool raw_gates = flags & F_RAW_GATES;
 
@@ -292,20 +319,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     };
 
     // Gated RMS norm (or plain copy) of the tokens [t0, t0 + tn): one wave per token.
+    // (z and the norm weights come from the registers prefetch_z filled)
     auto epilogue = [&](int t0, int tn) {
-        for (int tt = wave; tt < tn; tt += NW) {
+#pragma unroll
+        for (int i = 0; i < ZT; ++i) {
+            const int tt = wave + i * NW;
+            if (tt >= tn)
+                break;
             const int64_t r = (int64_t)b * p.T + t0 + tt;
             const int64_t obase = (r * Hv + h) * DV;
-            if (flags & F_GATED_NORM) {
+            if (gated) {
                 float ss = 0.f;
                 for (int j = lane; j < DV; j += 64)
                     ss += o_s[tt][j] * o_s[tt][j];
                 ss = group_sum<64>(ss);
                 const float inv = rsqrtf(ss / (float)DV + hc.norm_eps);
-                for (int j = lane; j < DV; j += 64) {
-                    const float zv = load_act(p.in.z, obase + j, p.in.z_dt);
-                    store_act(p.out, obase + j, p.out_dt,
-                              o_s[tt][j] * inv * p.in.norm_w[j] * silu_f(zv));
+#pragma unroll
+                for (int m = 0; m < ZJ; ++m) {
+                    const int j = lane + 64 * m;
+                    if (j < DV) {
+                        const float zv = word_to_f32(zw[i][m], obase + j, p.in.z_dt);
+                        store_act(p.out, obase + j, p.out_dt, o_s[tt][j] * inv * nw[m] * silu_f(zv));
+                    }
                 }
             } else {
                 for (int j = lane; j < DV; j += 64)
@@ -322,6 +357,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
             load_group(t, min(p.T - t, kTokGroup));
             __syncthreads();
             epilogue(t - kTokGroup, kTokGroup);
+            prefetch_z(t, min(p.T - t, kTokGroup));
             conv_group(min(p.T - t, kTokGroup));
             __syncthreads();
         }
