@@ -74,6 +74,7 @@ struct PrefillParams {
     int32_t *chunk_start;  // [num_chunks] first packed token row
     int32_t *chunk_len;    // [num_chunks] tokens in the chunk (1..64)
     int32_t *seq_chunk0;   // [N] index of each sequence's first chunk
+    int32_t *seq_order;    // [N] sequences longest first (the carry's order)
     uint16_t *qn;          // [num_chunks][Hk][64][dk]   f16, normalised q rows
     uint16_t *knT;         // [num_chunks][Hk][dk][64]   f16, normalised k, transposed
     uint16_t *wmat;        // [num_chunks][Hv][64][dk]   f16, W = T diag(beta*gamma) K

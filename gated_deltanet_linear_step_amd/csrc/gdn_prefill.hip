@@ -84,7 +84,8 @@ static_assert(perm_idx(perm_pos(21)) == 21 && perm_pos(perm_idx(13)) == 13, "per
 // ---------------------------------------------------------------- workspace
 
 struct WsLayout {
-    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, qn, knT, wmat, umat, aqk, gcum, onorm, total;
+    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, seq_order, qn, knT, wmat, umat, aqk, gcum, onorm,
+        total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -102,6 +103,7 @@ WsLayout ws_layout(int Hk, int Hv, int64_t MC, int N, int64_t total_tokens, bool
     L.chunk_start = take(sizeof(int32_t) * MC);
     L.chunk_len = take(sizeof(int32_t) * MC);
     L.seq_chunk0 = take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    L.seq_order = take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     L.qn = take(sizeof(uint16_t) * MC * Hk * C * DH);
     L.knT = take(sizeof(uint16_t) * MC * Hk * DH * C);
     L.wmat = take(sizeof(uint16_t) * MC * Hv * C * DH);
@@ -151,6 +153,24 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
         if (threadIdx.x == 255)
             base_s += scan[255];
         __syncthreads();
+    }
+    // The carry takes sequences longest first (its workgroups are the sequential
+    // chains; starting the long ones first shortens the whole call). Up to 256
+    // sequences are ranked by chunk count (ties by index); more keep their order.
+    if (p.N <= 256) {
+        const int i = threadIdx.x;
+        const int nc = i < p.N ? (p.cu[i + 1] - p.cu[i] + C - 1) / C : -1;
+        scan[i] = nc;
+        __syncthreads();
+        if (i < p.N) {
+            int rank = 0;
+            for (int j = 0; j < p.N; ++j)
+                rank += scan[j] > nc || (scan[j] == nc && j < i);
+            p.seq_order[rank] = i;
+        }
+    } else {
+        for (int i = threadIdx.x; i < p.N; i += 256)
+            p.seq_order[i] = i;
     }
 }
 
@@ -690,7 +710,7 @@ __global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
     const int part = (id >> 3) % NG;
     if (group >= p.N * Hv)
         return;
-    const int seq = group / Hv, h = group % Hv;
+    const int seq = p.seq_order[group / Hv], h = group % Hv;
     const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
     const int dvw = part * 16 * NW;  // the workgroup's first dv row
     const int lane = threadIdx.x & 63;
@@ -891,6 +911,7 @@ void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
     p.chunk_start = reinterpret_cast<int32_t *>(b + L.chunk_start);
     p.chunk_len = reinterpret_cast<int32_t *>(b + L.chunk_len);
     p.seq_chunk0 = reinterpret_cast<int32_t *>(b + L.seq_chunk0);
+    p.seq_order = reinterpret_cast<int32_t *>(b + L.seq_order);
     p.qn = reinterpret_cast<uint16_t *>(b + L.qn);
     p.knT = reinterpret_cast<uint16_t *>(b + L.knT);
     p.wmat = reinterpret_cast<uint16_t *>(b + L.wmat);
