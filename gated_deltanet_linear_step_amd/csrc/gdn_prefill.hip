@@ -921,6 +921,20 @@ void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
     p.onorm = reinterpret_cast<float *>(b + L.onorm);
 }
 
+template <int NW>
+void launch_carry(const PrefillParams &p, int64_t groups, hipStream_t s)
+{
+    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
+    const dim3 cblock(64 * NW);
+    const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
+    switch (omode) {
+    case kOutNorm: hipLaunchKernelGGL((carry_kernel<NW, kOutNorm>), cgrid, cblock, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((carry_kernel<NW, DT_F32>), cgrid, cblock, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((carry_kernel<NW, DT_F16>), cgrid, cblock, 0, s, p); break;
+    default: hipLaunchKernelGGL((carry_kernel<NW, DT_BF16>), cgrid, cblock, 0, s, p); break;
+    }
+}
+
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {
     if (p.num_chunks == 0)
@@ -932,20 +946,20 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
     case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
     }
-#ifndef GDN_CARRY_NW
-#define GDN_CARRY_NW 2
-#endif
-    constexpr int NW = GDN_CARRY_NW;  // dv slices (waves) per carry workgroup
+    // Carry: 2 dv slices (waves) per workgroup while the (sequence, head) pairs
+    // leave CUs idle (the per-chunk chain is shortest with 2 waves sharing a CU's
+    // LDS); 4 once 2-wave workgroups would need more than one round of CUs (each
+    // takes a whole CU's LDS), which halves the rounds.
     const int64_t groups = (int64_t)p.N * p.hc.Hv;
-    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
-    const dim3 cblock(64 * NW);
-    const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
-    switch (omode) {
-    case kOutNorm: hipLaunchKernelGGL((carry_kernel<NW, kOutNorm>), cgrid, cblock, 0, s, p); break;
-    case DT_F32: hipLaunchKernelGGL((carry_kernel<NW, DT_F32>), cgrid, cblock, 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((carry_kernel<NW, DT_F16>), cgrid, cblock, 0, s, p); break;
-    default: hipLaunchKernelGGL((carry_kernel<NW, DT_BF16>), cgrid, cblock, 0, s, p); break;
-    }
+    int cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    if (groups * (DH / 32) > cus)
+        launch_carry<4>(p, groups, s);
+    else
+        launch_carry<2>(p, groups, s);
     if (p.hc.flags & F_GATED_NORM) {
         const int64_t rows = (int64_t)p.total * p.hc.Hv;
         hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);

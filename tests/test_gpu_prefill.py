@@ -162,6 +162,27 @@ def test_ragged_lengths_including_empty(head_map):
         assert maxabs(f64(st[i]), S) <= TOL_STATE
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_many_sequences_four_slice_carry_workgroups(gated):
+    """Enough (sequence, head) pairs that the carry packs 4 dv slices per workgroup
+    (2-slice workgroups would need more than one round of CUs); ragged lengths,
+    empty ones included, every head compared."""
+    lengths = [(37 * i) % 150 for i in range(24)]  # 0 .. 148, two empties
+    P = synth.prefill(seed=15, lengths=lengths, Hk=2, Hv=4, head_map=synth.TILED,
+                      state_std=0.05, with_z=gated)
+    assert len(lengths) * 4 * (128 // 32) > 256  # past one round of 2-slice workgroups
+    out, st = run_prefill(P, gated=gated)
+    torch.cuda.synchronize()
+    for i, n in enumerate(lengths):
+        lo = int(P["cu_seqlens"][i])
+        if n == 0:
+            assert torch.equal(st[i].cpu(), P["state"][i]), "empty sequence changed its state"
+            continue
+        y, S = oracle_seq(P, i, f64(P["state"][i]), gated=gated)
+        assert maxabs(f64(out[lo:lo + n]), y) <= TOL_OUT
+        assert maxabs(f64(st[i]), S) <= TOL_STATE
+
+
 @pytest.mark.parametrize("act", [torch.float32, torch.float16])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_prefill_dtypes_and_gated_norm(act, out_dtype):
