@@ -138,3 +138,34 @@ def test_fused_layer_slots_and_out_of_range_slot():
     for s in (0, 2, 3):  # slots no sequence named: both states untouched
         assert torch.equal(pool[s], pool0[s])
         assert torch.all(cs_out[s] == 5.0)
+
+
+@pytest.mark.parametrize("B", [1, 32])
+def test_fused_layer_deep_model_shapes_hv48(B):
+    # Hk=16, Hv=48: two of the independently seeded layers of the 48-layer stack,
+    # through the launch the 48-layer benchmark leg uses
+    for layer in (0, 47):
+        W = to_dev(synth.decode_batch(seed=4 * 1000 + layer, B=B, Hk=16, Hv=48,
+                                      head_map=synth.TILED))
+        cs_out = torch.empty_like(W["conv_state_d"])
+        out = run_fused(W, T=1, B=B, cs_in=W["conv_state_d"], cs_out=cs_out,
+                        out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        y, cs, S = oracle_layer(W, B=B, T=1)
+        assert maxabs(f64(out).reshape(y.shape), y) <= TOL
+        assert maxabs(f64(W["state_d"]), S) <= TOL
+        assert maxabs(f64(cs_out), cs) == 0.0
+
+
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_fused_layer_multi_token_verify_b64(T):
+    # the benchmark's multi-token leg: B=64 sequences, T tokens each in one call
+    B = 64
+    W = to_dev(synth.decode_batch(seed=20 + T, B=B, T=T, head_map=synth.TILED))
+    cs_out = torch.empty_like(W["conv_state_d"])
+    out = run_fused(W, T=T, B=B, cs_in=W["conv_state_d"], cs_out=cs_out)
+    torch.cuda.synchronize()
+    y, cs, S = oracle_layer(W, B=B, T=T)
+    assert maxabs(f64(out).reshape(y.shape), y) <= TOL
+    assert maxabs(f64(W["state_d"]), S) <= TOL
+    assert maxabs(f64(cs_out), cs) == 0.0
