@@ -354,11 +354,13 @@ def prefill_bench(torch, ops, synth, *, lengths=(4096,), head_map=None, state_st
 
 def counter_pass(torch, ops, synth, steps=10, copy_mib=256):
     """For HBM-byte counters: `steps` steps of each decode leg of the headline
-    workload (fused layer, two-launch step), then `steps` copies of copy_mib MiB
+    workload (fused layer, two-launch step), 4 calls of the T=4096 prefill, then
+    `steps` copies of copy_mib MiB
     (read and written once each: 2 * copy_mib MiB of traffic per dispatch), whose
     counter readings calibrate the decode kernels'."""
     args = argparse.Namespace(warmup=2, steps=steps)
     decode_bench(args, torch, ops, synth)
+    prefill_bench(torch, ops, synth, calls=3, warmup=1)
     n = copy_mib * 2 ** 20 // 4
     src = torch.randn(n, device="cuda:0")
     dst = torch.empty_like(src)
