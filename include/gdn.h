@@ -109,7 +109,8 @@ typedef struct gdn_inputs {
     const float *decay_param, *dt_bias;
     /* no GDN_RAW_GATES: g (log decay, <= 0 in a real layer) and beta [tokens][Hv] f32 */
     const float *g, *beta;
-    /* GDN_GATED_NORM: z [tokens][Hv][dv] contiguous in z_dtype; norm_weight [dv] f32 */
+    /* GDN_GATED_NORM: z [tokens][Hv][dv] contiguous in z_dtype, 4-byte aligned;
+     * norm_weight [dv] f32 */
     const void *z;
     int32_t z_dtype;
     const float *norm_weight;
@@ -161,7 +162,8 @@ gdn_status gdn_conv_update(int32_t channels, int32_t kernel_size, int32_t num_se
  *                   and output rows untouched.
  *   num_slots       number of state slots (>= B when state_slots is NULL)
  *   out_dtype, out  [B*T][Hv][dv]; may not alias any input or the state
- * Errors: NULL, SHAPE, UNSUPPORTED (dims, dtype), OVERFLOW, ALIGN (state), LAUNCH.
+ * Errors: NULL, SHAPE, UNSUPPORTED (dims, dtype), OVERFLOW, ALIGN (q/k/v groups of 4
+ * elements; a, b, g, beta, z and norm_weight to 4 bytes; the state to 16 bytes), LAUNCH.
  * ------------------------------------------------------------------------- */
 gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
                            const gdn_inputs *in, float *state, const int32_t *state_slots,

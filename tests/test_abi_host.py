@@ -93,6 +93,8 @@ def test_decode_validation():
     assert decode(inp=inputs(g=None)) == NULL               # gates needed without RAW_GATES
     assert decode(d=dims(flags=ops.RAW_GATES)) == NULL      # a, b, decay, dt_bias missing
     assert decode(d=dims(flags=ops.GATED_NORM)) == NULL     # z, norm weight missing
+    assert decode(d=dims(flags=ops.GATED_NORM),
+                  inp=inputs(z=vp(P16 + 2), norm_weight=vp(P16))) == ALIGN  # z read as words
     assert decode(inp=inputs(q_stride=100)) == SHAPE        # narrower than Hk*dk
     assert decode(inp=inputs(q=vp(P16 + 2))) == ALIGN       # not 4-element aligned
     assert decode(inp=inputs(k_stride=1026)) == ALIGN
