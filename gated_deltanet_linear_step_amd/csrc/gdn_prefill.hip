@@ -27,12 +27,16 @@
 //                      prefix sums, T = (I + A)^-1 in f32 (16x16 diagonal blocks by
 //                      substitution, off-diagonal blocks by f32 MFMA block
 //                      products), U and W (f16 MFMA), Aqk and the decay rows.
-//  3. carry_kernel  -- per (sequence, v-head, 16-row slice of dv), sequential
-//                      over the sequence's chunks, one wave per slice: the slice's
-//                      S^T stays in MFMA accumulators (f32), rounded to f16 as the
-//                      B operand of W S^T and Q S^T; D enters the state update and
-//                      the output as f16 hi + lo pairs. Each chunk's operands are
-//                      copied global -> LDS one chunk ahead.
+//  3. carry         -- per (sequence, v-head, 16-row slice of dv), sequential
+//                      over the sequence's chunks: the slice's S^T stays in MFMA
+//                      accumulators (f32), rounded to f16 as the B operand of
+//                      W S^T and Q S^T; D enters the state update and the output
+//                      as f16 hi + lo pairs. Two copy waves per workgroup bring
+//                      each chunk's operands global -> LDS one chunk ahead.
+//                      carry_split_kernel (few sequences: latency bound) gives
+//                      each slice a compute wave for the recurrence and an output
+//                      wave for O; carry_kernel (many sequences: throughput
+//                      bound) does both in one wave per slice.
 //  4. norm_kernel   -- gated RMS norm of the f32 core output (optional).
 
 #include "gdn_device.h"
@@ -693,11 +697,12 @@ __device__ __forceinline__ void store_rows(const PrefillParams &p, int tok0, int
 //   O  = scale gamma Q S^T + (-scale Aqk)(-D)      -D as an f16 hi + lo pair
 //   S^T <- gamma_last S^T + K^T (D e)           D e as an f16 hi + lo pair
 // with e_t = exp(G_last - G_t). The chunk's operands arrive in LDS through
-// asynchronous global->LDS copies issued one chunk ahead into a two-slot ring
-// shared by the workgroup's waves; outputs are stored one chunk late. One
-// barrier per chunk.
+// asynchronous global->LDS copies that two copy waves issue one chunk ahead
+// into a two-slot ring (so the compute waves never stall behind a burst of
+// vector-memory issues); outputs are stored one chunk late. One barrier per
+// chunk.
 template <int NW, int OUT>
-__global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
+__global__ __launch_bounds__(64 * (NW + 2), 1) void carry_kernel(PrefillParams p)
 {
     __shared__ __attribute__((aligned(16))) ChunkImage<NW> img[2];
 
@@ -724,15 +729,26 @@ __global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
         return;  // empty sequence: state untouched
     const int c0 = p.seq_chunk0[seq];
 
+    if (wave >= NW) {
+        // copy waves: every chunk's operands, one chunk ahead, into the ring
+        const int cw = wave - NW;
+        const CopyOffsets<2, NW> co = copy_offsets<2, NW>(cw, lane);
+        issue_chunk_copy<2, NW>(img[0], p, co, c0, h, kh, dvw, cw, lane);
+        for (int ci = 0; ci < nch; ++ci) {
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): chunk ci has landed
+            __builtin_amdgcn_s_barrier();
+            if (ci + 1 < nch)
+                issue_chunk_copy<2, NW>(img[(ci + 1) & 1], p, co, c0 + ci + 1, h, kh, dvw, cw, lane);
+        }
+        return;
+    }
+
     // ST[m][r] = S[dvl][16m + 4lg + r]
     float *Sg = p.state + (((int64_t)seq * Hv + h) * DH + dvl) * DH + 4 * lg;
     f32x4 ST[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
         ST[m] = *reinterpret_cast<const f32x4 *>(Sg + 16 * m);
-
-    const CopyOffsets<NW, NW> co = copy_offsets<NW, NW>(wave, lane);
-    issue_chunk_copy<NW, NW>(img[0], p, co, c0, h, kh, dvw, wave, lane);
 
     // per-lane byte offsets of the swizzled operand reads
     int wq[4], ka[2], uo[4];
@@ -754,14 +770,12 @@ __global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
 
     auto step = [&](auto slot, int ci) {
         constexpr int SL = decltype(slot)::value;
-        // this chunk's copies (issued one chunk ago) have landed in every wave,
-        // and every wave is done reading the slot the next copies overwrite
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+        // this chunk's copies (issued one chunk ago) have landed, and every wave
+        // is done reading the slot the next copies overwrite
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         if (ci > 0)
             store_rows<OUT>(p, prev_tok0, prev_n, h, orow, lane_off, lg, Oprev);
-        if (ci + 1 < nch)
-            issue_chunk_copy<NW, NW>(img[SL ^ 1], p, co, c0 + ci + 1, h, kh, dvw, wave, lane);
         const ChunkImage<NW> &cur = img[SL];
         // The phases below are kept in source order (scheduling fences) so that
         // each phase's LDS operand reads are in flight during the previous
@@ -787,11 +801,12 @@ __global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
             sb[ks] = pack_tiles(ST[2 * ks], ST[2 * ks + 1]);
         __builtin_amdgcn_sched_barrier(0);
 
-        // phase 2: P' products, with the state update's K^T operands read behind them
+        // phase 2: P' products (consecutive ones into different accumulators),
+        // with the state update's K^T operands read behind them
         half8 kb[8][2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int j = i >> 2, ks = i & 3;
+            const int j = i & 3, ks = i >> 2;
             Pn[j] = mfma16(wa[j][ks], sb[ks], Pn[j]);
             kb[i >> 1][i & 1] = img_half8(cur.kt, ka[i & 1] + (i >> 1) * 2048);
             __builtin_amdgcn_sched_barrier(0);
@@ -823,13 +838,14 @@ __global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
         half8 qa[4][4], aa[6];
         f32x4 gm[4];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 8; ++m)
             ST[m] *= gl;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                ST[m] = mfma16(kb[m][ks], dh[ks], ST[m]);
-                ST[m] = mfma16(kb[m][ks], dl[ks], ST[m]);
-                const int i = 2 * m + ks;  // 16 Q reads, then Aqk and the gamma rows
+        for (int i2 = 0; i2 < 32; ++i2) {
+            const int m = i2 & 7, ks = i2 >> 4;
+            ST[m] = mfma16(kb[m][ks], (i2 >> 3) & 1 ? dl[ks] : dh[ks], ST[m]);
+            if (i2 & 1) {
+                const int i = i2 >> 1;  // 16 Q reads, then Aqk and the gamma rows
                 qa[i >> 2][i & 3] = img_half8(cur.q, wq[i & 3] + (i >> 2) * 4096);
                 if (i < 6)
                     aa[i] = img_half8(cur.aq, ka[i < 2 ? 0 : (i & 1)] + (i < 2 ? i : (i + 2) >> 1) * 2048);
@@ -870,6 +886,220 @@ __global__ __launch_bounds__(64 * NW, 1) void carry_kernel(PrefillParams p)
 #pragma unroll
     for (int m = 0; m < 8; ++m)
         *reinterpret_cast<f32x4 *>(Sg + 16 * m) = ST[m];
+}
+
+// Carry with the output products moved off the state's chain. Per 16-row dv
+// slice a compute wave runs the recurrence (P' = W S^T - U, D, S^T update) and
+// an output wave forms O = scale gamma Q S^T + (-scale Aqk)(-D) from the
+// state and -D the compute wave leaves in LDS; two copy waves keep the operand
+// ring one chunk ahead. Two barriers per chunk: A (chunk landed, state
+// published) and B (-D published).
+template <int NW, int OUT>
+__global__ __launch_bounds__(64 * (2 * NW + 2), 1) void carry_split_kernel(PrefillParams p)
+{
+    __shared__ __attribute__((aligned(16))) ChunkImage<NW> img[2];
+    // per slice: [0..3] S^T as the f16 B operand, [4..5] -D hi, [6..7] -D lo
+    __shared__ __attribute__((aligned(16))) half8 xs[NW][8][64];
+
+    const HeadCfg &hc = p.hc;
+    const int Hv = hc.Hv;
+    constexpr int NG = DH / (16 * NW);
+    const int id = blockIdx.x;
+    const int group = (id & 7) + 8 * (id / (8 * NG));
+    const int part = (id >> 3) % NG;
+    if (group >= p.N * Hv)
+        return;
+    const int seq = p.seq_order[group / Hv], h = group % Hv;
+    const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
+    const int dvw = part * 16 * NW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    const int start = p.cu[seq];
+    const int len = p.cu[seq + 1] - start;
+    const int nch = (len + C - 1) / C;
+    if (nch == 0)
+        return;
+    const int c0 = p.seq_chunk0[seq];
+
+    if (wave >= 2 * NW) {
+        const int cw = wave - 2 * NW;
+        const CopyOffsets<2, NW> co = copy_offsets<2, NW>(cw, lane);
+        issue_chunk_copy<2, NW>(img[0], p, co, c0, h, kh, dvw, cw, lane);
+        for (int ci = 0; ci < nch; ++ci) {
+            __builtin_amdgcn_s_waitcnt(0x0070);  // chunk ci has landed
+            __builtin_amdgcn_s_barrier();        // A
+            if (ci + 1 < nch)
+                issue_chunk_copy<2, NW>(img[(ci + 1) & 1], p, co, c0 + ci + 1, h, kh, dvw, cw, lane);
+            __builtin_amdgcn_s_barrier();        // B
+        }
+        return;
+    }
+
+    const int sl = wave < NW ? wave : wave - NW;  // slice within the workgroup
+    const int dvl = dvw + sl * 16 + li;
+    int wq[4], ka[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        wq[ks] = li * 256 + 16 * ((4 * ks + lg) ^ li);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+        ka[ks] = li * 128 + 16 * ((4 * ks + lg) ^ ((li >> 1) & 7));
+    half8 *xw = &xs[sl][0][lane];  // xw[64 * i] is entry i of this lane
+
+    if (wave < NW) {
+        // ---- compute wave
+        float *Sg = p.state + (((int64_t)seq * Hv + h) * DH + dvl) * DH + 4 * lg;
+        f32x4 ST[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            ST[m] = *reinterpret_cast<const f32x4 *>(Sg + 16 * m);
+        int uo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            uo[j] = (sl * 16 + li) * 256 + 16 * ((4 * j + lg) ^ li);
+        half8 sb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            sb[ks] = pack_tiles(ST[2 * ks], ST[2 * ks + 1]);
+            xw[64 * ks] = sb[ks];
+        }
+
+        auto step = [&](auto slot) {
+            constexpr int SL = decltype(slot)::value;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the state is published
+            __builtin_amdgcn_s_barrier();        // A
+            const ChunkImage<NW> &cur = img[SL];
+            half8 wa[4][4];
+            f32x4 Pn[4], er[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Pn[j] = img_f32x4(cur.u, uo[j]);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    wa[j][ks] = img_half8(cur.w, wq[ks] + j * 4096);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                er[j] = *reinterpret_cast<const f32x4 *>(&cur.gd[C + 16 * j + 4 * lg]);
+            const f32x4 g3 = *reinterpret_cast<const f32x4 *>(&cur.gd[48 + 4 * lg]);
+            __builtin_amdgcn_sched_barrier(0);
+
+            half8 kb[8][2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = i & 3, ks = i >> 2;
+                Pn[j] = mfma16(wa[j][ks], sb[ks], Pn[j]);
+                kb[i >> 1][i & 1] = img_half8(cur.kt, ka[i & 1] + (i >> 1) * 2048);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            half8 dh[2], dl[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 a = Pn[2 * ks] * er[2 * ks], b = Pn[2 * ks + 1] * er[2 * ks + 1];
+                const half8 dn = pack_tiles(Pn[2 * ks], Pn[2 * ks + 1]);
+                dh[ks] = pack_tiles(a, b);
+                f32x4 ar, br, pr, qr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ar[i] = a[i] - (float)dh[ks][i];
+                    br[i] = b[i] - (float)dh[ks][4 + i];
+                    pr[i] = Pn[2 * ks][i] - (float)dn[i];
+                    qr[i] = Pn[2 * ks + 1][i] - (float)dn[4 + i];
+                }
+                dl[ks] = pack_tiles(ar, br);
+                xw[64 * (4 + ks)] = dn;
+                xw[64 * (6 + ks)] = pack_tiles(pr, qr);
+            }
+            const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g3[3]), 48));
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): -D is published
+            __builtin_amdgcn_s_barrier();        // B
+
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                ST[m] *= gl;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const int m = i & 7, ks = i >> 4;
+                ST[m] = mfma16(kb[m][ks], (i >> 3) & 1 ? dl[ks] : dh[ks], ST[m]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                sb[ks] = pack_tiles(ST[2 * ks], ST[2 * ks + 1]);
+                xw[64 * ks] = sb[ks];
+            }
+        };
+        for (int ci = 0; ci < nch; ci += 2) {
+            step(Slot<0>{});
+            if (ci + 1 < nch)
+                step(Slot<1>{});
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            *reinterpret_cast<f32x4 *>(Sg + 16 * m) = ST[m];
+        return;
+    }
+
+    // ---- output wave
+    const int64_t orow = (int64_t)Hv * DH;
+    constexpr int ES = OUT == DT_F32 || OUT == kOutNorm ? 4 : 2;
+    const uint32_t lane_off = (uint32_t)((4 * lg * orow + dvl) * ES);
+    auto ostep = [&](auto slot, int ci) {
+        constexpr int SL = decltype(slot)::value;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();  // A
+        const ChunkImage<NW> &cur = img[SL];
+        half8 sbr[4], qa[4][4], aa[6];
+        f32x4 gm[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            sbr[ks] = xw[64 * ks];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            qa[i & 3][i >> 2] = img_half8(cur.q, wq[i >> 2] + (i & 3) * 4096);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            gm[j] = *reinterpret_cast<const f32x4 *>(&cur.gd[2 * C + 16 * j + 4 * lg]);
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            aa[i] = img_half8(cur.aq, ka[i < 2 ? 0 : (i & 1)] + (i < 2 ? i : (i + 2) >> 1) * 2048);
+        f32x4 qs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qs[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = i & 3, ks = i >> 2;
+            qs[j] = mfma16(qa[j][ks], sbr[ks], qs[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qs[j] *= gm[j];
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();  // B
+        half8 dn[2], dnl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            dn[ks] = xw[64 * (4 + ks)];
+            dnl[ks] = xw[64 * (6 + ks)];
+        }
+        // Aqk tiles (j, ks) with ks <= j / 2, in aa order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+#pragma unroll
+        for (int part2 = 0; part2 < 2; ++part2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (2 * ks <= j)
+                        qs[j] = mfma16(aa[j < 2 ? j : 2 + 2 * (j - 2) + ks], part2 ? dnl[ks] : dn[ks], qs[j]);
+        store_rows<OUT>(p, start + ci * C, min(C, len - ci * C), h, orow, lane_off, lg, qs);
+    };
+    for (int ci = 0; ci < nch; ci += 2) {
+        ostep(Slot<0>{}, ci);
+        if (ci + 1 < nch)
+            ostep(Slot<1>{}, ci + 1);
+    }
 }
 
 // ---------------------------------------------------------------- 4. gated norm
@@ -922,10 +1152,24 @@ void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
 }
 
 template <int NW>
+void launch_carry_split(const PrefillParams &p, int64_t groups, hipStream_t s)
+{
+    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
+    const dim3 cblock(64 * (2 * NW + 2));
+    const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
+    switch (omode) {
+    case kOutNorm: hipLaunchKernelGGL((carry_split_kernel<NW, kOutNorm>), cgrid, cblock, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((carry_split_kernel<NW, DT_F32>), cgrid, cblock, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((carry_split_kernel<NW, DT_F16>), cgrid, cblock, 0, s, p); break;
+    default: hipLaunchKernelGGL((carry_split_kernel<NW, DT_BF16>), cgrid, cblock, 0, s, p); break;
+    }
+}
+
+template <int NW>
 void launch_carry(const PrefillParams &p, int64_t groups, hipStream_t s)
 {
     const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
-    const dim3 cblock(64 * NW);
+    const dim3 cblock(64 * (NW + 2));
     const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
     switch (omode) {
     case kOutNorm: hipLaunchKernelGGL((carry_kernel<NW, kOutNorm>), cgrid, cblock, 0, s, p); break;
@@ -946,20 +1190,24 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
     case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
     }
-    // Carry: 2 dv slices (waves) per workgroup while the (sequence, head) pairs
-    // leave CUs idle (the per-chunk chain is shortest with 2 waves sharing a CU's
-    // LDS); 4 once 2-wave workgroups would need more than one round of CUs (each
-    // takes a whole CU's LDS), which halves the rounds.
+    // Carry shape (each workgroup takes a whole CU's LDS): while one round of
+    // workgroups covers every dv slice the call is bound by the per-chunk chain,
+    // so the split carry runs with 1 slice per workgroup (8 per head) or, when
+    // that would take two rounds, 2; beyond that it is throughput bound and the
+    // 4-slice carry, which reads each chunk's shared operands once for 4 slices,
+    // is fastest.
     const int64_t groups = (int64_t)p.N * p.hc.Hv;
     int cus = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (groups * (DH / 32) > cus)
-        launch_carry<4>(p, groups, s);
+    if (groups * (DH / 16) <= cus)
+        launch_carry_split<1>(p, groups, s);
+    else if (groups * (DH / 32) <= cus)
+        launch_carry_split<2>(p, groups, s);
     else
-        launch_carry<2>(p, groups, s);
+        launch_carry<4>(p, groups, s);
     if (p.hc.flags & F_GATED_NORM) {
         const int64_t rows = (int64_t)p.total * p.hc.Hv;
         hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);

@@ -165,12 +165,36 @@ def test_ragged_lengths_including_empty(head_map):
 @pytest.mark.parametrize("gated", [False, True])
 def test_many_sequences_four_slice_carry_workgroups(gated):
     """Enough (sequence, head) pairs that the carry packs 4 dv slices per workgroup
-    (2-slice workgroups would need more than one round of CUs); ragged lengths,
-    empty ones included, every head compared."""
+    (the split carry's 2-slice workgroups would need more than one round of CUs);
+    ragged lengths, empty ones included, every head compared."""
     lengths = [(37 * i) % 150 for i in range(24)]  # 0 .. 148, two empties
     P = synth.prefill(seed=15, lengths=lengths, Hk=2, Hv=4, head_map=synth.TILED,
                       state_std=0.05, with_z=gated)
     assert len(lengths) * 4 * (128 // 32) > 256  # past one round of 2-slice workgroups
+    out, st = run_prefill(P, gated=gated)
+    torch.cuda.synchronize()
+    for i, n in enumerate(lengths):
+        lo = int(P["cu_seqlens"][i])
+        if n == 0:
+            assert torch.equal(st[i].cpu(), P["state"][i]), "empty sequence changed its state"
+            continue
+        y, S = oracle_seq(P, i, f64(P["state"][i]), gated=gated)
+        assert maxabs(f64(out[lo:lo + n]), y) <= TOL_OUT
+        assert maxabs(f64(st[i]), S) <= TOL_STATE
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_two_slice_split_carry_workgroups(gated):
+    """Between 33 and 64 (sequence, head) pairs: the split carry with 2 dv slices
+    per workgroup (1-slice workgroups would need two rounds of CUs); ragged
+    lengths across several chunks, an empty sequence, every head compared."""
+    lengths = [(53 * i + 40) % 300 for i in range(12)]  # 5 .. 270 tokens
+    lengths[3] = 192  # whole chunks only
+    lengths[5] = 0
+    P = synth.prefill(seed=16, lengths=lengths, Hk=2, Hv=4, head_map=synth.GROUPED,
+                      state_std=0.05, with_z=gated)
+    groups = len(lengths) * 4
+    assert groups * (128 // 16) > 256 >= groups * (128 // 32)
     out, st = run_prefill(P, gated=gated)
     torch.cuda.synchronize()
     for i, n in enumerate(lengths):
