@@ -180,6 +180,23 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
 
 // ---------------------------------------------------------------- 2. prep
 
+// One gate input element (16-bit or f32) as two 16-bit loads that never leave the
+// element, so the load is issued without a branch on the dtype and its latency
+// can be hidden: an f32 element's halves, or a 16-bit element read twice.
+struct GateWord {
+    uint16_t lo, hi;
+};
+__device__ __forceinline__ GateWord load_gate(const void *p, int64_t idx, int dt)
+{
+    const uint16_t *b = static_cast<const uint16_t *>(p) + (dt == DT_F32 ? 2 * idx : idx);
+    return GateWord{b[0], b[dt == DT_F32 ? 1 : 0]};
+}
+__device__ __forceinline__ float gate_value(GateWord w, int dt)
+{
+    const float f32 = __uint_as_float(((uint32_t)w.hi << 16) | w.lo);
+    return dt == DT_F32 ? f32 : (dt == DT_BF16 ? bf16_bits_to_f32(w.lo) : f16_bits_to_f32(w.lo));
+}
+
 // One workgroup per (chunk, k-head): the normalised q/k rows, K K^T, Q K^T and
 // the workspace's Q and K^T are formed once and serve the Hv/Hk v-heads that
 // read this k-head, which the workgroup then takes in turn (gates, A and Aqk,
@@ -208,6 +225,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     static_assert(sizeof(VT) >= C * KP * 2, "VT holds the K remainders");
     float(*Am)[AP] = reinterpret_cast<float(*)[AP]>(X1);
     float(*Pm)[36] = reinterpret_cast<float(*)[36]>(X2);
+    // -scale Aqk (f16, token slots in the permuted order), staged behind Pm for a
+    // coalesced copy to the workspace
+    uint16_t(*Aqs)[C] = reinterpret_cast<uint16_t(*)[C]>(X2 + 32 * 36 * 4);
+    static_assert(32 * 36 * 4 + C * C * 2 <= C * KP * 2, "X2 holds Pm and the staged Aqk");
 
     const HeadCfg &hc = p.hc;
     const ActInputs &in = p.in;
@@ -231,6 +252,26 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             vr[i] = load_raw4<QT>(in.v, (int64_t)(tok0 + min(t, n - 1)) * in.v_stride + (int64_t)h * DH + 4 * dq);
         }
     };
+
+    // gate inputs of one v-head (wave 0, lane = token; lanes past the chunk's end
+    // re-read its last token and are zeroed when used), fetched one v-head ahead
+    const bool raw = flags & F_RAW_GATES;
+    const void *gsrc_a = raw ? in.a : static_cast<const void *>(in.g);
+    const void *gsrc_b = raw ? in.b : static_cast<const void *>(in.beta);
+    const int gdt = raw ? in.ab_dt : DT_F32;
+    GateWord ga, gb;
+    float gdp = 0.f, gdb = 0.f;
+    auto load_gates = [&](int h) {
+        const int64_t gi = (int64_t)(tok0 + min(lane, n - 1)) * Hv + h;
+        ga = load_gate(gsrc_a, gi, gdt);
+        gb = load_gate(gsrc_b, gi, gdt);
+        if (raw) {
+            gdp = in.decay_param[h];
+            gdb = in.dt_bias[h];
+        }
+    };
+    if (wave == 0)
+        load_gates(vhead(0));
 
     // -- rows of k and q: wave w loads tokens 16w .. 16w+15, 32 lanes per row;
     // rows past the chunk's end re-read its last row and are zeroed after.
@@ -339,19 +380,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
         __syncthreads();
         // -- gates and their prefix sums (wave 0, lane = token)
         if (wave == 0) {
-            float g = 0.f, beta = 0.f;
-            if (lane < n) {
-                const int64_t gi = (int64_t)(tok0 + lane) * Hv + h;
-                if (flags & F_RAW_GATES) {
-                    const float dp = in.decay_param[h];
-                    const float rate = hc.decay_kind == 0 ? -expf(dp) : dp;
-                    g = rate * softplus_f(load_act(in.a, gi, in.ab_dt) + in.dt_bias[h]);
-                    beta = sigmoid_f(load_act(in.b, gi, in.ab_dt));
-                } else {
-                    g = in.g[gi];
-                    beta = in.beta[gi];
-                }
+            float g = gate_value(ga, gdt), beta = gate_value(gb, gdt);
+            if (raw) {
+                const float rate = hc.decay_kind == 0 ? -expf(gdp) : gdp;
+                g = rate * softplus_f(g + gdb);
+                beta = sigmoid_f(beta);
             }
+            if (lane >= n)
+                g = beta = 0.f;
+            if (j + 1 < G)
+                load_gates(vhead(j + 1));
             float Gc = g;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -382,9 +420,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             load_v(vr, vhead(j + 1));  // the next v-head's rows, in flight from here
         __syncthreads();
 
-        // -- A (strictly lower, f32) into X1; decayed, masked, scaled -Q K^T to the workspace
+        // -- A (strictly lower, f32) into X1; decayed, masked, scaled -Q K^T staged in X2
         {
-            uint16_t *aq = p.aqk + ((int64_t)chunk * Hv + h) * C * C;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
@@ -392,14 +429,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
                     const int t = wave * 16 + lg * 4 + r, s = jj * 16 + li;
                     const float dg = s <= t ? __expf(G_s[t] - G_s[s]) : 0.f;
                     Am[t][s] = s < t ? beta_s[t] * dg * gram[jj][r] : 0.f;
-                    aq[t * C + perm_pos(s)] = f32_to_f16_bits(-hc.scale * dg * qk[jj][r]);
+                    Aqs[t][perm_pos(s)] = f32_to_f16_bits(-hc.scale * dg * qk[jj][r]);
                 }
             }
         }
         __syncthreads();
 
         // -- T = (I + A)^-1 in place. (a) the four 16x16 diagonal blocks by forward
-        // substitution: wave 0, lane = (block, column).
+        // substitution: wave 0, lane = (block, column); meanwhile waves 1-3 copy
+        // the staged -scale Aqk to the workspace.
+        if (wave > 0) {
+            uint16_t *aq = p.aqk + ((int64_t)chunk * Hv + h) * C * C;
+            for (int e = threadIdx.x - 64; e < C * C / 8; e += 192) {
+                const int t = e / (C / 8), c8 = (e % (C / 8)) * 8;
+                *reinterpret_cast<uint4 *>(aq + t * C + c8) = *reinterpret_cast<const uint4 *>(&Aqs[t][c8]);
+            }
+        }
         if (wave == 0) {
             const int b0 = (lane >> 4) * 16, c = lane & 15;
             float x[16];
