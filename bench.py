@@ -217,6 +217,48 @@ def verify_bench(torch, ops, synth, Ts=(2, 4, 8), calls=200, warmup=20):
                 **res)
 
 
+HEAD_SHAPES = ((32, 32), (64, 64), (128, 128), (64, 128), (128, 64), (128, 256), (256, 128))
+
+
+def head_shapes_bench(torch, ops, synth, calls=300, warmup=30):
+    """The fused decode layer at every built (dk, dv) head shape: B=64 x 1 token,
+    Hk=16, Hv=32, tiled map, bf16 N(0,1) activations, fp32 state; state GB/s over
+    back-to-back launches (the state is read and written once per launch)."""
+    dev = torch.device("cuda:0")
+    B, Hk, Hv = 64, 16, 32
+    res = {}
+    for dk, dv in HEAD_SHAPES:
+        W = synth.decode_batch(seed=30 + dk + dv, B=B, Hk=Hk, Hv=Hv, dk=dk, dv=dv,
+                               head_map=synth.TILED)
+        S = {k: (v.to(dev).contiguous() if hasattr(v, "to") else v) for k, v in W.items()}
+        cb = torch.empty_like(S["conv_state"])
+        out = torch.empty((B, Hv, dv), dtype=torch.bfloat16, device=dev)
+        x, QK = S["x"], Hk * dk
+        calls_ = [ops.prepare_decode_layer(
+            x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:], S["state"], S["conv_w"], ci, co, out,
+            Hk=Hk, Hv=Hv, dk=dk, dv=dv, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
+            decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"])
+            for ci, co in ((S["conv_state"], cb), (cb, S["conv_state"]))]
+        for i in range(warmup):
+            calls_[i & 1].launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(calls):
+            calls_[i & 1].launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        state_bytes = 2 * B * Hv * dv * dk * 4
+        gbps = state_bytes / (ms * 1e-3) / 1e9
+        res[f"{dk}x{dv}"] = dict(us_per_launch=ms * 1e3, state_GBps=gbps,
+                                 pct_hbm_peak=100 * gbps / HBM_PEAK_GBS)
+        del S, W, calls_
+    return dict(workload="fused decode layer per head shape (dk x dv): B=64 x 1 token, Hk=16, "
+                         "Hv=32, tiled map, bf16 N(0,1), fp32 state, back-to-back launches",
+                **res)
+
+
 def deep_model_bench(torch, ops, synth, batches=(1, 32), layers=48, steps=(100, 20)):
     """Deep-model decode: Hk=16, Hv=48, d=128, `layers` layers applied in sequence per
     token, each with its own seeded taps, gates, norm, state and conv window (seed
@@ -410,7 +452,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true",
-                    help="skip the multi-token and the 48-layer decode legs")
+                    help="skip the multi-token, 48-layer and head-shape decode legs")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: a few decode steps, then a plain "
                          "256 MiB device copy of known size (the counters' calibration)")
@@ -450,6 +492,8 @@ def main():
         line["verify"] = verify_bench(torch, ops, synth)
         print("[bench] deep-model decode, 48 layers, B=1 and B=32", file=sys.stderr, flush=True)
         line["deep_model"] = deep_model_bench(torch, ops, synth)
+        print("[bench] decode layer per head shape", file=sys.stderr, flush=True)
+        line["head_shapes"] = head_shapes_bench(torch, ops, synth)
     if not args.no_prefill:
         print("[bench] prefill T=4096", file=sys.stderr, flush=True)
         pre = prefill_bench(

@@ -402,21 +402,38 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
 
 }  // namespace
 
+// Built head shapes (dk, dv) and their waves per workgroup. A row's dk floats sit
+// in dk/4 lanes (so dk/4 divides 64), each wave holds at most 64 rows, and the
+// fused layer gives every one of its 2 dk + dv conv channels a thread. A lane's
+// share of the state must fit its registers: 16 float4 pieces at 8 waves (256
+// VGPRs per lane), 8 at 16 waves (128). dk = dv = 256 would need 16 pieces at
+// 16 waves (768 conv channels) and is not built.
 bool decode_supported(int dk, int dv)
 {
-    return (dk == 128 && dv == 128) || (dk == 64 && dv == 64) || (dk == 32 && dv == 32);
+    return (dk == 128 && dv == 128) || (dk == 64 && dv == 64) || (dk == 32 && dv == 32) ||
+           (dk == 64 && dv == 128) || (dk == 128 && dv == 64) || (dk == 128 && dv == 256) ||
+           (dk == 256 && dv == 128);
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
 {
     if (p.B == 0)
         return hipSuccess;
-    if (p.hc.dk == 128 && p.hc.dv == 128)
+    const int dk = p.hc.dk, dv = p.hc.dv;
+    if (dk == 128 && dv == 128)
         return launch_decode_t<128, 128, GDN_DECODE_NW>(p, s);
-    if (p.hc.dk == 64 && p.hc.dv == 64)
+    if (dk == 64 && dv == 64)
         return launch_decode_t<64, 64, 4>(p, s);
-    if (p.hc.dk == 32 && p.hc.dv == 32)
+    if (dk == 32 && dv == 32)
         return launch_decode_t<32, 32, 4>(p, s);
+    if (dk == 64 && dv == 128)
+        return launch_decode_t<64, 128, 8>(p, s);
+    if (dk == 128 && dv == 64)
+        return launch_decode_t<128, 64, 8>(p, s);
+    if (dk == 128 && dv == 256)
+        return launch_decode_t<128, 256, 8>(p, s);
+    if (dk == 256 && dv == 128)
+        return launch_decode_t<256, 128, 16>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -139,20 +139,24 @@ def test_deep_model_layer_shapes_hv48(B):
 
 # ------------------------------------------------------------------ small shapes, maps, dtypes
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+# every built (dk, dv) head shape
+HEAD_SHAPES = [(32, 32), (64, 64), (128, 128), (64, 128), (128, 64), (128, 256), (256, 128)]
+
+
+@pytest.mark.parametrize("dk,dv", HEAD_SHAPES)
 @pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
 @pytest.mark.parametrize("T", [1, 11])
-def test_core_given_gates_shapes(d, head_map, T):
-    rng = np.random.default_rng(100 + d + T + head_map)
+def test_core_given_gates_shapes(dk, dv, head_map, T):
+    rng = np.random.default_rng(100 + dk + 3 * dv + T + head_map)
     B, Hk, Hv = 3, 2, 4
-    q = torch.from_numpy(rng.normal(size=(B * T, Hk, d)).astype(np.float32))
-    k = torch.from_numpy(rng.normal(size=(B * T, Hk, d)).astype(np.float32))
-    v = torch.from_numpy(rng.normal(size=(B * T, Hv, d)).astype(np.float32))
+    q = torch.from_numpy(rng.normal(size=(B * T, Hk, dk)).astype(np.float32))
+    k = torch.from_numpy(rng.normal(size=(B * T, Hk, dk)).astype(np.float32))
+    v = torch.from_numpy(rng.normal(size=(B * T, Hv, dv)).astype(np.float32))
     g = torch.from_numpy(-np.abs(rng.normal(size=(B * T, Hv))).astype(np.float32))
     beta = torch.from_numpy(rng.uniform(0, 1, size=(B * T, Hv)).astype(np.float32))
-    S0 = torch.from_numpy(rng.normal(0, 0.1, size=(B, Hv, d, d)).astype(np.float32))
+    S0 = torch.from_numpy(rng.normal(0, 0.1, size=(B, Hv, dv, dk)).astype(np.float32))
     st = S0.to(DEV)
-    out = ops.decode_step(q.to(DEV), k.to(DEV), v.to(DEV), st, Hk=Hk, Hv=Hv, dk=d, dv=d,
+    out = ops.decode_step(q.to(DEV), k.to(DEV), v.to(DEV), st, Hk=Hk, Hv=Hv, dk=dk, dv=dv,
                           head_map=head_map, batch=B, tokens_per_seq=T, g=g.to(DEV),
                           beta=beta.to(DEV), l2norm_qk=True)
     torch.cuda.synchronize()
@@ -162,6 +166,21 @@ def test_core_given_gates_shapes(d, head_map, T):
                              g=f64(g[sl]), beta=f64(beta[sl]), l2norm_qk=True)
         assert maxabs(f64(out[sl]), yo) <= TOL
         assert maxabs(f64(st[bi]), So) <= TOL
+
+
+@pytest.mark.parametrize("dk,dv", HEAD_SHAPES[3:])
+@pytest.mark.parametrize("T", [1, 3])
+def test_two_launch_layer_head_shapes(dk, dv, T):
+    """conv update + decode step with L2 norm, raw gates and the gated norm at the
+    non-square and 256-wide head shapes."""
+    B = 2
+    W = to_dev(synth.decode_batch(seed=60 + dk + dv + T, B=B, Hk=2, Hv=4, dk=dk, dv=dv, T=T))
+    out = run_layer(W, T=T, B=B)
+    torch.cuda.synchronize()
+    y, cs, S = oracle_layer(W, B=B, T=T)
+    assert maxabs(f64(out).reshape(y.shape), y) <= TOL
+    assert maxabs(f64(W["state_d"]), S) <= TOL
+    assert maxabs(f64(W["conv_state_d"]), cs) == 0.0
 
 
 @pytest.mark.parametrize("act", [torch.float32, torch.float16, torch.bfloat16])

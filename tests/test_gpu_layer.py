@@ -78,13 +78,15 @@ def test_fused_layer_b64_steps_1_and_8():
             assert maxabs(f64(bufs[0]), cs_ref) == 0.0, f"step {step} conv state"
 
 
-@pytest.mark.parametrize("d,Hk,Hv", [(128, 2, 4), (64, 2, 2), (32, 1, 4)])
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(128, 128, 2, 4), (64, 64, 2, 2), (32, 32, 1, 4),
+                                         (64, 128, 2, 2), (128, 64, 2, 4), (128, 256, 2, 4),
+                                         (256, 128, 1, 2)])
 @pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
 @pytest.mark.parametrize("T", [1, 3, 9, 17])
-def test_fused_layer_shapes_maps_tokens(d, Hk, Hv, head_map, T):
+def test_fused_layer_shapes_maps_tokens(dk, dv, Hk, Hv, head_map, T):
     B = 3
-    W = to_dev(synth.decode_batch(seed=40 + T + d, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d, T=T,
-                                  head_map=head_map))
+    W = to_dev(synth.decode_batch(seed=40 + T + dk + 2 * dv, B=B, Hk=Hk, Hv=Hv, dk=dk, dv=dv,
+                                  T=T, head_map=head_map))
     cs_out = torch.full_like(W["conv_state_d"], 9.0)
     out = run_fused(W, T=T, B=B, cs_in=W["conv_state_d"], cs_out=cs_out)
     torch.cuda.synchronize()
