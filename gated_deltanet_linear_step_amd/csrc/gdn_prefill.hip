@@ -130,11 +130,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
     __syncthreads();
     for (int i0 = 0; i0 < p.N; i0 += 256) {
         const int i = i0 + threadIdx.x;
-        int start = 0, len = 0;
-        if (i < p.N) {
-            start = p.cu[i];
-            len = p.cu[i + 1] - start;
-        }
+        const int len = i < p.N ? p.cu[i + 1] - p.cu[i] : 0;
         const int nc = (len + C - 1) / C;
         scan[threadIdx.x] = nc;
         __syncthreads();
@@ -144,14 +140,27 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
             scan[threadIdx.x] += v;
             __syncthreads();
         }
-        const int first = base_s + scan[threadIdx.x] - nc;
-        if (i < p.N) {
-            p.seq_chunk0[i] = first;
-            for (int c = 0; c < nc; ++c) {
-                p.chunk_seq[first + c] = i;
-                p.chunk_start[first + c] = start + c * C;
-                p.chunk_len[first + c] = min(C, len - c * C);
+        if (i < p.N)
+            p.seq_chunk0[i] = base_s + scan[threadIdx.x] - nc;
+        // this block's chunks, one per thread: chunk c (counted from the block's
+        // first) belongs to the first sequence whose inclusive count exceeds c
+        const int total = scan[255];
+        for (int c = threadIdx.x; c < total; c += 256) {
+            int lo = 0, hi = 255;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (scan[mid] > c)
+                    hi = mid;
+                else
+                    lo = mid + 1;
             }
+            const int k = c - (lo ? scan[lo - 1] : 0);  // chunk within its sequence
+            const int seq = i0 + lo;
+            const int s0 = p.cu[seq], sl = p.cu[seq + 1] - s0;
+            const int g = base_s + c;
+            p.chunk_seq[g] = seq;
+            p.chunk_start[g] = s0 + k * C;
+            p.chunk_len[g] = min(C, sl - k * C);
         }
         __syncthreads();
         if (threadIdx.x == 255)

@@ -207,6 +207,25 @@ def test_two_slice_split_carry_workgroups(gated):
         assert maxabs(f64(st[i]), S) <= TOL_STATE
 
 
+def test_more_than_256_sequences():
+    """300 short ragged sequences (empty ones included): the chunk table is built in
+    blocks of 256 sequences, and past 256 the carry keeps the sequences' order."""
+    rng = np.random.default_rng(17)
+    lengths = [int(x) for x in rng.choice([0, 1, 5, 63, 64, 65, 100], size=300)]
+    P = synth.prefill(seed=17, lengths=lengths, Hk=1, Hv=2, head_map=synth.TILED,
+                      state_std=0.05)
+    out, st = run_prefill(P)
+    torch.cuda.synchronize()
+    for i, n in enumerate(lengths):
+        lo = int(P["cu_seqlens"][i])
+        if n == 0:
+            assert torch.equal(st[i].cpu(), P["state"][i]), "empty sequence changed its state"
+            continue
+        y, S = oracle_seq(P, i, f64(P["state"][i]))
+        assert maxabs(f64(out[lo:lo + n]), y) <= TOL_OUT
+        assert maxabs(f64(st[i]), S) <= TOL_STATE
+
+
 @pytest.mark.parametrize("act", [torch.float32, torch.float16])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_prefill_dtypes_and_gated_norm(act, out_dtype):
