@@ -221,8 +221,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     __shared__ __attribute__((aligned(16))) unsigned char X2[C * KP * 2];
     __shared__ __attribute__((aligned(16))) _Float16 VT[DH][TP];  // v, [dv][token slot] (per v-head)
     __shared__ __attribute__((aligned(16))) _Float16 KT[DH][TP];  // k, [dk slot][token slot]
-    __shared__ float G_s[C], beta_s[C], bg_s[C];
+    __shared__ __attribute__((aligned(16))) float G_s[C], beta_s[C], bg_s[C];
     static_assert(C * AP * 4 >= C * KP * 2, "X1 holds both the K rows and A / T");
+    static_assert((AP * 4) % 16 == 0, "A / T rows are 16-byte aligned");
     static_assert(C * KP * 2 >= 32 * 36 * 4, "X2 holds the Q rows and the 32x32 scratch");
 
     _Float16(*Kh)[KP] = reinterpret_cast<_Float16(*)[KP]>(X1);
@@ -521,15 +522,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
         // 16w..; the contraction runs over token slots, so T's columns are taken in
         // slot order, each scaled by its token's beta (U) or beta gamma (W)
         {
+            // slots ks*32 + 8lg .. +7 are tokens ks*32 + 4lg .. +3 and ks*32 + 16 + 4lg .. +3:
+            // two runs of four, read as 16-byte vectors
             half8 tu[2], tw[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int s = perm_idx(ks * 32 + lg * 8 + i);
-                    const float tv = Am[wave * 16 + li][s];
-                    tu[ks][i] = (_Float16)(tv * beta_s[s]);
-                    tw[ks][i] = (_Float16)(tv * bg_s[s]);
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int s0 = ks * 32 + 16 * hf + 4 * lg;
+                    const f32x4 tv = *reinterpret_cast<const f32x4 *>(&Am[wave * 16 + li][s0]);
+                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(&beta_s[s0]);
+                    const f32x4 bg = *reinterpret_cast<const f32x4 *>(&bg_s[s0]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        tu[ks][4 * hf + i] = (_Float16)(tv[i] * bt[i]);
+                        tw[ks][4 * hf + i] = (_Float16)(tv[i] * bg[i]);
+                    }
                 }
             float *ud = p.umat + ((int64_t)chunk * Hv + h) * DH * C;
             _Float16(*Wl)[KP] = reinterpret_cast<_Float16(*)[KP]>(X2);  // W rows, staged
