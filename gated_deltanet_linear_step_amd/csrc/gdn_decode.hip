@@ -30,6 +30,10 @@
 //    of tokens into LDS, and the waves take q, k, v from there. The window after
 //    the call goes to the output conv state; q/k channels are written by one
 //    workgroup per k-head.
+//  * Several tokens per sequence (fused layer): each token's norms, k.q and gates
+//    are computed once per conv group, by one wave per token, and shared through
+//    LDS instead of by every lane for every token. The operations are the
+//    single-token path's, so a call and any split of it agree bit for bit.
 
 #include "gdn_device.h"
 #include "gdn_kernels.h"
@@ -134,8 +138,17 @@ struct ConvLane {
     }
 };
 
-template <int DK, int DV, int NW, int QT, int CK>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
+// Two 8-wave workgroups per CU (4 waves per SIMD, 128 VGPRs) for the shapes whose
+// state share fits; the larger shapes take the registers they need.
+template <int DK, int DV, int NW>
+constexpr int decode_min_waves() { return NW == 8 && DK * DV <= 128 * 128 ? 4 : 1; }
+
+// GS (fused layer, several tokens per sequence): the per-token scalars (q/k norms,
+// k.q, gates) are computed once per token of a conv group and shared through LDS,
+// instead of by every lane for every token. The arithmetic is the per-lane one,
+// operation for operation, so a call and any split of it agree bit for bit.
+template <int DK, int DV, int NW, int QT, int CK, bool GS>
+__global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void decode_kernel(DecodeParams p)
 {
     constexpr int LPR = DK / 4;       // lanes holding one row
     constexpr int RPI = 64 / LPR;     // rows per wave-wide load
@@ -148,6 +161,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     constexpr int NCH = 2 * DK + DV;  // conv channels one workgroup reads
     static_assert(CK == 0 || NCH <= NW * 64, "one conv channel per thread");
     __shared__ float y_s[CK > 0 ? kTokGroup : 1][CK > 0 ? NCH : 1];  // conv outputs
+    // per token of a conv group: 1/|k|, 1/|q|, k.q of the normalised pair, alpha, beta
+    __shared__ float sc_s[GS ? kTokGroup : 1][5];
+    constexpr int GT = (kTokGroup + NW - 1) / NW;  // group tokens per wave
 
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv;
@@ -176,7 +192,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     // are counted in order, so the prologue math can run while the state is in
     // flight, and each row piece is processed as soon as it lands.
     TokenRaw<QT> tr;
-    load_token<DK, DV, QT, CK == 0>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
+    // fused layer: each wave fetches the gate words of its tokens of a conv group
+    // (tokens wave, wave + NW, ...) with the group's inputs; otherwise every lane
+    // fetches its token's activations
+    const bool raw_g = flags & F_RAW_GATES;
+    const void *gsa = raw_g ? p.in.a : static_cast<const void *>(p.in.g);
+    const void *gsb = raw_g ? p.in.b : static_cast<const void *>(p.in.beta);
+    const int gdt0 = raw_g ? p.in.ab_dt : DT_F32;
+    GateWord gwa[GT], gwb[GT];
+    auto load_group_gates = [&](int t0, int tn) {
+#pragma unroll
+        for (int i = 0; i < GT; ++i) {
+            const int64_t r = (int64_t)b * p.T + t0 + min(wave + i * NW, tn - 1);
+            gwa[i] = load_gate(gsa, r * Hv + h, gdt0);
+            gwb[i] = load_gate(gsb, r * Hv + h, gdt0);
+        }
+    };
+    if constexpr (GS)
+        load_group_gates(0, min(p.T, kTokGroup));
+    else
+        load_token<DK, DV, QT, CK == 0>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
     // fused conv: this thread's channel (q, k or v), its raw input of the first
     // token group, weights and window, all issued before the state loads
     const int64_t nch = 2 * (int64_t)hc.Hk * DK + (int64_t)Hv * DV;
@@ -260,20 +295,81 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
                     if (tt < tn)
                         xr[tt] = load_raw1<QT>(xsrc, ((int64_t)b * p.T + t0 + tt) * xstride + xoff);
             }
+            if constexpr (GS)
+                load_group_gates(t0, tn);
+        }
+    };
+    const int gdt = raw_gates ? p.in.ab_dt : DT_F32;
+    // the gates of one token from its raw words
+    // the gates of one token from its a and b (or g and beta) inputs; both token
+    // paths decode the same element to the same float first
+    auto gates = [&](float ga, float gb, float &alpha, float &beta) {
+        float g;
+        if (raw_gates) {
+            g = dec_rate * softplus_f(ga + dtb);
+            beta = sigmoid_f(gb);
+        } else {
+            g = ga;
+            beta = gb;
+        }
+        alpha = expf(g);
+    };
+    // The per-token scalars of one token from its convolved q and k (kk, qq: this
+    // lane's four elements) and gate words: the norms scale kk and qq in place.
+    auto token_scalars = [&](float4 &kk, float4 &qq, float ga, float gb, float &ik, float &iq,
+                             float &kq, float &alpha, float &beta) {
+        ik = 1.f;
+        iq = 1.f;
+        if (flags & F_L2NORM) {
+            const float sk = group_sum<LPR>(dot4(kk, kk));
+            const float sq = group_sum<LPR>(dot4(qq, qq));
+            ik = rsqrtf(sk + hc.l2_eps);
+            iq = rsqrtf(sq + hc.l2_eps);
+            kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
+            qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
+        }
+        gates(ga, gb, alpha, beta);
+        kq = group_sum<LPR>(dot4(kk, qq));
+    };
+    // GS: the scalars of a conv group's tokens, wave w taking tokens w, w + NW, ...
+    // (every lane computes, lane 0 writes sc_s)
+    auto group_scalars = [&](int tn) {
+        if constexpr (GS) {
+#pragma unroll
+            for (int i = 0; i < GT; ++i) {
+                const int tt = wave + i * NW;
+                if (tt < tn) {
+                    float4 qq = *reinterpret_cast<const float4 *>(&y_s[tt][col]);
+                    float4 kk = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col]);
+                    float ik, iq, kq, alpha, beta;
+                    token_scalars(kk, qq, gate_value(gwa[i], gdt), gate_value(gwb[i], gdt), ik, iq, kq,
+                                  alpha, beta);
+                    if (lane == 0) {
+                        sc_s[tt][0] = ik;
+                        sc_s[tt][1] = iq;
+                        sc_s[tt][2] = kq;
+                        sc_s[tt][3] = alpha;
+                        sc_s[tt][4] = beta;
+                    }
+                }
+            }
         }
     };
     if constexpr (CK > 0) {
         conv_group(min(p.T, kTokGroup));
         __syncthreads();
+        if constexpr (GS) {
+            group_scalars(min(p.T, kTokGroup));
+            __syncthreads();
+        }
     }
-    const int gdt = raw_gates ? p.in.ab_dt : DT_F32;
 
     // One token through this wave's rows: prologue (norms, gates), then the two
     // reductions, the update and the read-out per row piece; outputs go to
     // o_s[tt] for the group epilogue.
     auto process_token = [&](int tt, int64_t r) {
         float4 kk, qq;
-        float vv;
+        float vv, alpha, beta, kq;
         if constexpr (CK > 0) {
             qq = *reinterpret_cast<const float4 *>(&y_s[tt][col]);
             kk = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col]);
@@ -283,32 +379,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
             qq = raw4_to_f32<QT>(tr.q);
             vv = raw1_to_f32<QT>(tr.v);
         }
-        if (flags & F_L2NORM) {
-            const float sk = group_sum<LPR>(dot4(kk, kk));
-            const float sq = group_sum<LPR>(dot4(qq, qq));
-            const float ik = rsqrtf(sk + hc.l2_eps), iq = rsqrtf(sq + hc.l2_eps);
-            kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
-            qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
-        }
-        const float ga = word_to_f32(tr.ga, r * Hv + h, gdt);
-        const float gb = word_to_f32(tr.gb, r * Hv + h, gdt);
-        float g, beta;
-        if (raw_gates) {
-            g = dec_rate * softplus_f(ga + dtb);
-            beta = sigmoid_f(gb);
+        if constexpr (GS) {
+            const float ik = sc_s[tt][0], iq = sc_s[tt][1];
+            if (flags & F_L2NORM) {
+                kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
+                qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
+            }
+            kq = sc_s[tt][2];
+            alpha = sc_s[tt][3];
+            beta = sc_s[tt][4];
         } else {
-            g = ga;
-            beta = gb;
+            float ik, iq;
+            token_scalars(kk, qq, word_to_f32(tr.ga, r * Hv + h, gdt), word_to_f32(tr.gb, r * Hv + h, gdt),
+                          ik, iq, kq, alpha, beta);
         }
-        const float alpha = expf(g);
-        const float kq = group_sum<LPR>(dot4(kk, qq));
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const float pk = group_sum<LPR>(dot4(S[i], kk));
             const float pq = group_sum<LPR>(dot4(S[i], qq));
             const float vj = __shfl(vv, sub + i * RPI, 64);
-            const float d = beta * (vj - alpha * pk);
-            const float o = hc.scale * (alpha * pq + d * kq);
+            const float d = beta * fmaf(-alpha, pk, vj);
+            const float o = hc.scale * fmaf(alpha, pq, d * kq);
             S[i].x = fmaf(alpha, S[i].x, d * kk.x);
             S[i].y = fmaf(alpha, S[i].y, d * kk.y);
             S[i].z = fmaf(alpha, S[i].z, d * kk.z);
@@ -331,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
             if (gated) {
                 float ss = 0.f;
                 for (int j = lane; j < DV; j += 64)
-                    ss += o_s[tt][j] * o_s[tt][j];
+                    ss = fmaf(o_s[tt][j], o_s[tt][j], ss);
                 ss = group_sum<64>(ss);
                 const float inv = rsqrtf(ss / (float)DV + hc.norm_eps);
 #pragma unroll
@@ -360,9 +451,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
             prefetch_z(t, min(p.T - t, kTokGroup));
             conv_group(min(p.T - t, kTokGroup));
             __syncthreads();
+            if constexpr (GS) {
+                group_scalars(min(p.T - t, kTokGroup));
+                __syncthreads();
+            }
         }
         const int64_t r = (int64_t)b * p.T + t;
-        load_token<DK, DV, QT, CK == 0>(tr, p, r, h, kh, col, vrow);
+        if constexpr (!GS)
+            load_token<DK, DV, QT, CK == 0>(tr, p, r, h, kh, col, vrow);
         process_token(tt, r);
     }
 #pragma unroll
@@ -379,15 +475,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p)
     epilogue(tlast0, p.T - tlast0);
 }
 
-template <int DK, int DV, int NW, int CK>
-void launch_decode_ck(const DecodeParams &p, hipStream_t s)
+template <int DK, int DV, int NW, int CK, bool GS>
+void launch_decode_gs(const DecodeParams &p, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)p.B * p.hc.Hv)), block(NW * 64);
     switch (p.in.qkv_dt) {
-    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK>), grid, block, 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK>), grid, block, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK, GS>), grid, block, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK, GS>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK, GS>), grid, block, 0, s, p); break;
     }
+}
+
+template <int DK, int DV, int NW, int CK>
+void launch_decode_ck(const DecodeParams &p, hipStream_t s)
+{
+    if constexpr (CK > 0) {
+        if (p.T > 1) {
+            launch_decode_gs<DK, DV, NW, CK, true>(p, s);
+            return;
+        }
+    }
+    launch_decode_gs<DK, DV, NW, CK, false>(p, s);
 }
 
 template <int DK, int DV, int NW>

@@ -104,6 +104,24 @@ __device__ __forceinline__ float word_to_f32(uint32_t w, int64_t idx, int dt)
     return dt == DT_F32 ? __uint_as_float(w) : (dt == DT_BF16 ? vbf16 : vf16);
 }
 
+// One gate input element (16-bit or f32) as two 16-bit loads that never leave the
+// element (an f32 element's halves, or a 16-bit element read twice), so the load
+// is issued without a branch on the dtype and never reads past the array's end;
+// the two halves are kept packed in one register.
+struct GateWord {
+    uint32_t bits;
+};
+__device__ __forceinline__ GateWord load_gate(const void *p, int64_t idx, int dt)
+{
+    const uint16_t *b = static_cast<const uint16_t *>(p) + (dt == DT_F32 ? 2 * idx : idx);
+    return GateWord{(uint32_t)b[0] | ((uint32_t)b[dt == DT_F32 ? 1 : 0] << 16)};
+}
+__device__ __forceinline__ float gate_value(GateWord w, int dt)
+{
+    const uint32_t lo = w.bits & 0xffffu;
+    return dt == DT_F32 ? __uint_as_float(w.bits) : (dt == DT_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo));
+}
+
 // Raw bits of four consecutive activations of compile-time dtype DT (8 bytes for
 // 16-bit types, 16 for f32) and their conversion.
 template <int DT>
@@ -199,9 +217,10 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// An explicit fused chain: every kernel that calls it rounds the same way
 __device__ __forceinline__ float dot4(float4 a, float4 b)
 {
-    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, a.x * b.x)));
 }
 
 // ---- gate activations (split-by-sign sigmoid, softplus with +-20 cut-overs) ----

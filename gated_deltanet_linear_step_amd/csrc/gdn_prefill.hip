@@ -189,23 +189,6 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillParams p)
 
 // ---------------------------------------------------------------- 2. prep
 
-// One gate input element (16-bit or f32) as two 16-bit loads that never leave the
-// element, so the load is issued without a branch on the dtype and its latency
-// can be hidden: an f32 element's halves, or a 16-bit element read twice.
-struct GateWord {
-    uint16_t lo, hi;
-};
-__device__ __forceinline__ GateWord load_gate(const void *p, int64_t idx, int dt)
-{
-    const uint16_t *b = static_cast<const uint16_t *>(p) + (dt == DT_F32 ? 2 * idx : idx);
-    return GateWord{b[0], b[dt == DT_F32 ? 1 : 0]};
-}
-__device__ __forceinline__ float gate_value(GateWord w, int dt)
-{
-    const float f32 = __uint_as_float(((uint32_t)w.hi << 16) | w.lo);
-    return dt == DT_F32 ? f32 : (dt == DT_BF16 ? bf16_bits_to_f32(w.lo) : f16_bits_to_f32(w.lo));
-}
-
 // One workgroup per (chunk, k-head): the normalised q/k rows, K K^T, Q K^T and
 // the workspace's Q and K^T are formed once and serve the Hv/Hk v-heads that
 // read this k-head, which the workgroup then takes in turn (gates, A and Aqk,
