@@ -105,7 +105,10 @@ typedef struct gdn_inputs {
     int64_t q_stride, k_stride, v_stride;
     int32_t qkv_dtype;      /* gdn_dtype of q, k, v */
     /* GDN_RAW_GATES: a, b [tokens][Hv] contiguous in ab_dtype; decay_param and
-     * dt_bias [Hv] f32. */
+     * dt_bias [Hv] f32. The decode reads 16-bit a, b by element pairs (the 4
+     * bytes from each even element index), so when tokens*Hv is odd the
+     * allocation must extend 2 bytes past the last element (allocations rounded
+     * to 4 bytes, as torch's are, satisfy this). */
     const void *a, *b;
     int32_t ab_dtype;
     const float *decay_param, *dt_bias;
