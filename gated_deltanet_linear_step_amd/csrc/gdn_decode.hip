@@ -11,8 +11,11 @@
 //
 // Design (HBM bound: 0.5 flop per state byte):
 //  * one workgroup per (sequence, v-head), NW waves; wave w owns value rows
-//    [w*DV/NW, (w+1)*DV/NW). A row's DK floats are spread over DK/4 lanes as one
-//    float4 each, so one dwordx4 wave load moves 64/(DK/4) whole rows (1 KiB).
+//    [w*DV/NW, (w+1)*DV/NW). A row's DK floats are spread over LPR lanes, each
+//    holding DK/(4 LPR) float4 pieces of it: lane r of a row holds the columns
+//    4r + 4 LPR m. One dwordx4 wave load moves piece m of 64/LPR rows, each as
+//    a contiguous 16 LPR-byte run. The row dot products then reduce over LPR
+//    lanes only (DPP within a row of 16 lanes when LPR <= 16, no LDS step).
 //  * every state row is loaded into VGPRs once per call, carried through all of
 //    the call's tokens (rows are independent), and stored once.
 //  * the two row dot products use the old state: S_j.k and S_j.q are reduced
@@ -78,21 +81,25 @@ __device__ __forceinline__ void store_state4(float *p, float4 s)
 // Activations of one token for one wave, as raw bits: the k and q pieces, the
 // two gate words (raw a/b or given g/beta) and one v element per lane. Loading
 // and converting are separate so the state loads can be issued in between.
-template <int QT>
+template <int QT, int PPR>
 struct TokenRaw {
-    Raw4<QT> k, q;
+    Raw4<QT> k[PPR], q[PPR];
     uint32_t ga, gb, v;
 };
 
-template <int DK, int DV, int QT, bool QKV = true>
-__device__ __forceinline__ void load_token(TokenRaw<QT> &t, const DecodeParams &p, int64_t r,
+// piece m of a lane that holds columns col + 4 LPR m of a row
+template <int DK, int DV, int QT, int PPR, int LPR, bool QKV = true>
+__device__ __forceinline__ void load_token(TokenRaw<QT, PPR> &t, const DecodeParams &p, int64_t r,
                                            int h, int kh, int col, int vrow)
 {
     const ActInputs &in = p.in;
     const int Hv = p.hc.Hv;
     if constexpr (QKV) {
-        t.k = load_raw4<QT>(in.k, r * in.k_stride + (int64_t)kh * DK + col);
-        t.q = load_raw4<QT>(in.q, r * in.q_stride + (int64_t)kh * DK + col);
+#pragma unroll
+        for (int m = 0; m < PPR; ++m) {
+            t.k[m] = load_raw4<QT>(in.k, r * in.k_stride + (int64_t)kh * DK + col + 4 * LPR * m);
+            t.q[m] = load_raw4<QT>(in.q, r * in.q_stride + (int64_t)kh * DK + col + 4 * LPR * m);
+        }
     }
     const bool raw = p.hc.flags & F_RAW_GATES;
     const int gdt = raw ? in.ab_dt : DT_F32;
@@ -138,6 +145,33 @@ struct ConvLane {
     }
 };
 
+// A lane's share of a row dot product over its PPR pieces, as one explicit fused
+// chain (for PPR = 1 it is dot4 itself)
+template <int PPR>
+__device__ __forceinline__ float dotn(const float4 *a, const float4 *b)
+{
+    float acc = dot4(a[0], b[0]);
+#pragma unroll
+    for (int m = 1; m < PPR; ++m) {
+        acc = fmaf(a[m].x, b[m].x, acc);
+        acc = fmaf(a[m].y, b[m].y, acc);
+        acc = fmaf(a[m].z, b[m].z, acc);
+        acc = fmaf(a[m].w, b[m].w, acc);
+    }
+    return acc;
+}
+
+// Lanes per state row: 16 for the 128-wide rows (two float4 pieces per lane, the
+// row sums stay within a 16-lane DPP row), dk/4 (one piece per lane) otherwise.
+// At 128 x 128, 16 lanes per row take about a sixth of the reduction steps of 32
+// (4 rows per lane with 2 x 4 DPP steps each, against 8 rows with 2 x 5 steps, one
+// of them through LDS) for 8 more VGPRs of k and q; 32 and 8 lanes spill.
+#ifndef GDN_DECODE_LPR128
+#define GDN_DECODE_LPR128 16
+#endif
+template <int DK, int DV>
+constexpr int decode_lpr() { return DK == 128 ? GDN_DECODE_LPR128 : DK / 4; }
+
 // Two 8-wave workgroups per CU (4 waves per SIMD, 128 VGPRs) for the shapes whose
 // state share fits; the larger shapes take the registers they need.
 template <int DK, int DV, int NW>
@@ -150,11 +184,13 @@ constexpr int decode_min_waves() { return NW == 8 && DK * DV <= 128 * 128 ? 4 : 
 template <int DK, int DV, int NW, int QT, int CK, bool GS>
 __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void decode_kernel(DecodeParams p)
 {
-    constexpr int LPR = DK / 4;       // lanes holding one row
-    constexpr int RPI = 64 / LPR;     // rows per wave-wide load
-    constexpr int RPW = DV / NW;      // rows per wave
-    constexpr int NI = RPW / RPI;     // float4 row pieces per lane
-    static_assert(DK % 4 == 0 && 64 % LPR == 0 && RPW % RPI == 0 && NI >= 1, "shape");
+    constexpr int LPR = decode_lpr<DK, DV>();  // lanes holding one row
+    constexpr int PPR = DK / (4 * LPR);        // float4 pieces of a row per lane
+    constexpr int RPI = 64 / LPR;              // rows per wave-wide load
+    constexpr int RPW = DV / NW;               // rows per wave
+    constexpr int RPL = RPW / RPI;             // rows per lane
+    constexpr int NI = RPL * PPR;              // float4 state pieces per lane
+    static_assert(DK % (4 * LPR) == 0 && 64 % LPR == 0 && RPW % RPI == 0 && RPL >= 1, "shape");
     static_assert(RPW <= 64, "one v value per lane covers the wave's rows");
 
     __shared__ float o_s[kTokGroup][DV];
@@ -191,7 +227,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     // Token 0's activations are issued before the state: vector-memory returns
     // are counted in order, so the prologue math can run while the state is in
     // flight, and each row piece is processed as soon as it lands.
-    TokenRaw<QT> tr;
+    TokenRaw<QT, PPR> tr;
     // fused layer: each wave fetches the gate words of its tokens of a conv group
     // (tokens wave, wave + NW, ...) with the group's inputs; otherwise every lane
     // fetches its token's activations
@@ -211,7 +247,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     if constexpr (GS)
         load_group_gates(0, min(p.T, kTokGroup));
     else
-        load_token<DK, DV, QT, CK == 0>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
+        load_token<DK, DV, QT, PPR, LPR, CK == 0>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
     // fused conv: this thread's channel (q, k or v), its raw input of the first
     // token group, weights and window, all issued before the state loads
     const int64_t nch = 2 * (int64_t)hc.Hk * DK + (int64_t)Hv * DV;
@@ -244,10 +280,10 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     __builtin_amdgcn_sched_barrier(0);  // keep the token loads ahead of the state loads
 
     float *Sg = p.state + ((int64_t)slot * Hv + h) * (int64_t)(DV * DK);
-    float4 S[NI];
+    float4 S[NI];  // S[r * PPR + m]: piece m of the lane's row r
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-        S[i] = load_state4(Sg + (row0 + i * RPI) * DK + col);
+        S[i] = load_state4(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR));
     // the gated norm's z and weights for the first token group, behind the state:
     // the epilogue then waits on nothing (branch-free: without the norm the loads
     // read the state's first word and are not used)
@@ -316,20 +352,26 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     };
     // The per-token scalars of one token from its convolved q and k (kk, qq: this
     // lane's four elements) and gate words: the norms scale kk and qq in place.
-    auto token_scalars = [&](float4 &kk, float4 &qq, float ga, float gb, float &ik, float &iq,
+    auto scale_vec = [&](float4 *x, float f) {
+#pragma unroll
+        for (int m = 0; m < PPR; ++m) {
+            x[m].x *= f; x[m].y *= f; x[m].z *= f; x[m].w *= f;
+        }
+    };
+    auto token_scalars = [&](float4 *kk, float4 *qq, float ga, float gb, float &ik, float &iq,
                              float &kq, float &alpha, float &beta) {
         ik = 1.f;
         iq = 1.f;
         if (flags & F_L2NORM) {
-            const float sk = group_sum<LPR>(dot4(kk, kk));
-            const float sq = group_sum<LPR>(dot4(qq, qq));
+            const float sk = group_sum<LPR>(dotn<PPR>(kk, kk));
+            const float sq = group_sum<LPR>(dotn<PPR>(qq, qq));
             ik = rsqrtf(sk + hc.l2_eps);
             iq = rsqrtf(sq + hc.l2_eps);
-            kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
-            qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
+            scale_vec(kk, ik);
+            scale_vec(qq, iq);
         }
         gates(ga, gb, alpha, beta);
-        kq = group_sum<LPR>(dot4(kk, qq));
+        kq = group_sum<LPR>(dotn<PPR>(kk, qq));
     };
     // GS: the scalars of a conv group's tokens, wave w taking tokens w, w + NW, ...
     // (every lane computes, lane 0 writes sc_s)
@@ -339,8 +381,12 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
             for (int i = 0; i < GT; ++i) {
                 const int tt = wave + i * NW;
                 if (tt < tn) {
-                    float4 qq = *reinterpret_cast<const float4 *>(&y_s[tt][col]);
-                    float4 kk = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col]);
+                    float4 qq[PPR], kk[PPR];
+#pragma unroll
+                    for (int m = 0; m < PPR; ++m) {
+                        qq[m] = *reinterpret_cast<const float4 *>(&y_s[tt][col + 4 * LPR * m]);
+                        kk[m] = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col + 4 * LPR * m]);
+                    }
                     float ik, iq, kq, alpha, beta;
                     token_scalars(kk, qq, gate_value(gwa[i], gdt), gate_value(gwb[i], gdt), ik, iq, kq,
                                   alpha, beta);
@@ -368,22 +414,28 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     // reductions, the update and the read-out per row piece; outputs go to
     // o_s[tt] for the group epilogue.
     auto process_token = [&](int tt, int64_t r) {
-        float4 kk, qq;
+        float4 kk[PPR], qq[PPR];
         float vv, alpha, beta, kq;
         if constexpr (CK > 0) {
-            qq = *reinterpret_cast<const float4 *>(&y_s[tt][col]);
-            kk = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col]);
+#pragma unroll
+            for (int m = 0; m < PPR; ++m) {
+                qq[m] = *reinterpret_cast<const float4 *>(&y_s[tt][col + 4 * LPR * m]);
+                kk[m] = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col + 4 * LPR * m]);
+            }
             vv = y_s[tt][2 * DK + vrow];
         } else {
-            kk = raw4_to_f32<QT>(tr.k);
-            qq = raw4_to_f32<QT>(tr.q);
+#pragma unroll
+            for (int m = 0; m < PPR; ++m) {
+                kk[m] = raw4_to_f32<QT>(tr.k[m]);
+                qq[m] = raw4_to_f32<QT>(tr.q[m]);
+            }
             vv = raw1_to_f32<QT>(tr.v);
         }
         if constexpr (GS) {
             const float ik = sc_s[tt][0], iq = sc_s[tt][1];
             if (flags & F_L2NORM) {
-                kk.x *= ik; kk.y *= ik; kk.z *= ik; kk.w *= ik;
-                qq.x *= iq; qq.y *= iq; qq.z *= iq; qq.w *= iq;
+                scale_vec(kk, ik);
+                scale_vec(qq, iq);
             }
             kq = sc_s[tt][2];
             alpha = sc_s[tt][3];
@@ -394,18 +446,22 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
                           ik, iq, kq, alpha, beta);
         }
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const float pk = group_sum<LPR>(dot4(S[i], kk));
-            const float pq = group_sum<LPR>(dot4(S[i], qq));
-            const float vj = __shfl(vv, sub + i * RPI, 64);
+        for (int rr = 0; rr < RPL; ++rr) {
+            float4 *Sr = &S[rr * PPR];
+            const float pk = group_sum<LPR>(dotn<PPR>(Sr, kk));
+            const float pq = group_sum<LPR>(dotn<PPR>(Sr, qq));
+            const float vj = __shfl(vv, sub + rr * RPI, 64);
             const float d = beta * fmaf(-alpha, pk, vj);
             const float o = hc.scale * fmaf(alpha, pq, d * kq);
-            S[i].x = fmaf(alpha, S[i].x, d * kk.x);
-            S[i].y = fmaf(alpha, S[i].y, d * kk.y);
-            S[i].z = fmaf(alpha, S[i].z, d * kk.z);
-            S[i].w = fmaf(alpha, S[i].w, d * kk.w);
+#pragma unroll
+            for (int m = 0; m < PPR; ++m) {
+                Sr[m].x = fmaf(alpha, Sr[m].x, d * kk[m].x);
+                Sr[m].y = fmaf(alpha, Sr[m].y, d * kk[m].y);
+                Sr[m].z = fmaf(alpha, Sr[m].z, d * kk[m].z);
+                Sr[m].w = fmaf(alpha, Sr[m].w, d * kk[m].w);
+            }
             if (col == 0)
-                o_s[tt][row0 + i * RPI] = o;
+                o_s[tt][row0 + rr * RPI] = o;
         }
     };
 
@@ -458,12 +514,12 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
         }
         const int64_t r = (int64_t)b * p.T + t;
         if constexpr (!GS)
-            load_token<DK, DV, QT, CK == 0>(tr, p, r, h, kh, col, vrow);
+            load_token<DK, DV, QT, PPR, LPR, CK == 0>(tr, p, r, h, kh, col, vrow);
         process_token(tt, r);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-        store_state4(Sg + (row0 + i * RPI) * DK + col, S[i]);
+        store_state4(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR), S[i]);
     if constexpr (CK > 0) {
         // the window after this call's tokens; q/k channels from one v-head per k-head
         const bool qk_writer = hc.head_map == 0 ? (h % (Hv / hc.Hk) == 0) : (h < hc.Hk);
@@ -511,7 +567,8 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
 }  // namespace
 
 // Built head shapes (dk, dv) and their waves per workgroup. A row's dk floats sit
-// in dk/4 lanes (so dk/4 divides 64), each wave holds at most 64 rows, and the
+// in 16 lanes for dk = 128 and in dk/4 lanes otherwise (that count divides 64),
+// each wave holds at most 64 rows, and the
 // fused layer gives every one of its 2 dk + dv conv channels a thread. A lane's
 // share of the state must fit its registers: 16 float4 pieces at 8 waves (256
 // VGPRs per lane), 8 at 16 waves (128). dk = dv = 256 would need 16 pieces at
