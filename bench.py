@@ -217,7 +217,8 @@ def verify_bench(torch, ops, synth, Ts=(2, 4, 8), calls=200, warmup=20):
                 **res)
 
 
-HEAD_SHAPES = ((32, 32), (64, 64), (128, 128), (64, 128), (128, 64), (128, 256), (256, 128))
+HEAD_SHAPES = ((32, 32), (64, 64), (96, 96), (128, 128), (64, 128), (128, 64), (128, 256),
+               (256, 128))
 
 
 def head_shapes_bench(torch, ops, synth, calls=300, warmup=30):

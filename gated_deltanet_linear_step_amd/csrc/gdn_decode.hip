@@ -169,13 +169,24 @@ __device__ __forceinline__ float dotn(const float4 *a, const float4 *b)
 #ifndef GDN_DECODE_LPR128
 #define GDN_DECODE_LPR128 16
 #endif
+// 256-wide rows: 32 lanes (two pieces each); 64 lanes spill at 16 waves.
+// 96-wide rows: 8 lanes (three pieces each), since 24 does not divide a wave.
+#ifndef GDN_DECODE_LPR256
+#define GDN_DECODE_LPR256 32
+#endif
 template <int DK, int DV>
-constexpr int decode_lpr() { return DK == 128 ? GDN_DECODE_LPR128 : DK / 4; }
+constexpr int decode_lpr()
+{
+    return DK == 128 ? GDN_DECODE_LPR128 : DK == 256 ? GDN_DECODE_LPR256 : DK == 96 ? 8 : DK / 4;
+}
 
 // Two 8-wave workgroups per CU (4 waves per SIMD, 128 VGPRs) for the shapes whose
 // state share fits; the larger shapes take the registers they need.
 template <int DK, int DV, int NW>
-constexpr int decode_min_waves() { return NW == 8 && DK * DV <= 128 * 128 ? 4 : 1; }
+constexpr int decode_min_waves()
+{
+    return NW == 8 && DK * DV <= 128 * 128 ? 4 : (NW == 6 ? 3 : 1);
+}
 
 // GS (fused layer, several tokens per sequence): the per-token scalars (q/k norms,
 // k.q, gates) are computed once per token of a conv group and shared through LDS,
@@ -567,17 +578,17 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
 }  // namespace
 
 // Built head shapes (dk, dv) and their waves per workgroup. A row's dk floats sit
-// in 16 lanes for dk = 128 and in dk/4 lanes otherwise (that count divides 64),
-// each wave holds at most 64 rows, and the
-// fused layer gives every one of its 2 dk + dv conv channels a thread. A lane's
-// share of the state must fit its registers: 16 float4 pieces at 8 waves (256
-// VGPRs per lane), 8 at 16 waves (128). dk = dv = 256 would need 16 pieces at
-// 16 waves (768 conv channels) and is not built.
+// in decode_lpr lanes (16 for dk = 128, 32 for 256, 8 for 96, dk/4 otherwise; the
+// count divides 64), each wave holds at most 64 rows, and the fused layer gives
+// every one of its 2 dk + dv conv channels a thread. A lane's share of the state
+// must fit its registers: 16 float4 pieces at 8 waves (256 VGPRs per lane), 8 at
+// 16 waves (128). dk = dv = 256 would need 16 pieces at 16 waves (768 conv
+// channels); built that way it spills about 300 bytes per lane, so it is not.
 bool decode_supported(int dk, int dv)
 {
     return (dk == 128 && dv == 128) || (dk == 64 && dv == 64) || (dk == 32 && dv == 32) ||
            (dk == 64 && dv == 128) || (dk == 128 && dv == 64) || (dk == 128 && dv == 256) ||
-           (dk == 256 && dv == 128);
+           (dk == 256 && dv == 128) || (dk == 96 && dv == 96);
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
@@ -599,6 +610,8 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
         return launch_decode_t<128, 256, 8>(p, s);
     if (dk == 256 && dv == 128)
         return launch_decode_t<256, 128, 16>(p, s);
+    if (dk == 96 && dv == 96)
+        return launch_decode_t<96, 96, 6>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -83,7 +83,8 @@ typedef struct gdn_dims {
     int32_t num_v_heads; /* Hv >= 1, Hv % Hk == 0 */
     int32_t head_dim_k;  /* dk */
     int32_t head_dim_v;  /* dv. Built (dk, dv): decode step and layer (32,32), (64,64),
-                            (128,128), (64,128), (128,64), (128,256), (256,128);
+                            (96,96), (128,128), (64,128), (128,64), (128,256),
+                            (256,128);
                             chunked prefill (128,128). Others: UNSUPPORTED. */
     int32_t head_map;    /* gdn_head_map */
     int32_t decay;       /* gdn_decay, used with GDN_RAW_GATES */

@@ -140,7 +140,8 @@ def test_deep_model_layer_shapes_hv48(B):
 # ------------------------------------------------------------------ small shapes, maps, dtypes
 
 # every built (dk, dv) head shape
-HEAD_SHAPES = [(32, 32), (64, 64), (128, 128), (64, 128), (128, 64), (128, 256), (256, 128)]
+HEAD_SHAPES = [(32, 32), (64, 64), (128, 128), (64, 128), (128, 64), (128, 256), (256, 128),
+               (96, 96)]
 
 
 @pytest.mark.parametrize("dk,dv", HEAD_SHAPES)
