@@ -103,8 +103,9 @@ __device__ __forceinline__ void load_token(TokenRaw<QT, PPR> &t, const DecodePar
     }
     const bool raw = p.hc.flags & F_RAW_GATES;
     const int gdt = raw ? in.ab_dt : DT_F32;
-    t.ga = load_word_nb(raw ? in.a : (const void *)in.g, r * Hv + h, gdt);
-    t.gb = load_word_nb(raw ? in.b : (const void *)in.beta, r * Hv + h, gdt);
+    const int64_t gi = r * Hv + h + vgpr_zero();  // a vector load (see vgpr_zero)
+    t.ga = load_word_nb(raw ? in.a : (const void *)in.g, gi, gdt);
+    t.gb = load_word_nb(raw ? in.b : (const void *)in.beta, gi, gdt);
     if constexpr (QKV)
         t.v = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DV + vrow);
 }
@@ -114,16 +115,42 @@ __device__ __forceinline__ void load_token(TokenRaw<QT, PPR> &t, const DecodePar
 // oldest input.
 template <int QT, int CK>
 struct ConvLane {
+    static constexpr int ES = QT == DT_F32 ? 4 : 2;  // bytes per element
     float w[CK], win[CK - 1];
+    // The channel's taps and window as loaded: one copy each of their contiguous
+    // bytes, kept as whole words. Element loads would be merged into wider ones
+    // and split again as they land, which makes the code wait for them right
+    // there; convert() splits the words after the state loads are issued.
+    uint32_t wr[(CK * ES + 3) / 4], winr[((CK - 1) * ES + 3) / 4];
 
     __device__ __forceinline__ void load(const DecodeParams &p, int64_t ch, int64_t sbase)
     {
+        __builtin_memcpy(wr, static_cast<const char *>(p.conv_w) + ch * CK * ES, CK * ES);
+        __builtin_memcpy(winr, static_cast<const char *>(p.conv_in) + sbase * ES, (CK - 1) * ES);
+    }
+    __device__ __forceinline__ void convert()
+    {
+        // the words enter here as opaque registers, so no part of the splitting
+        // can be moved up next to the loads
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(wr) / 4); ++i)
+            asm volatile("" : "+v"(wr[i]));
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(winr) / 4); ++i)
+            asm volatile("" : "+v"(winr[i]));
 #pragma unroll
         for (int m = 0; m < CK; ++m)
-            w[m] = raw1_to_f32<QT>(load_raw1<QT>(p.conv_w, ch * CK + m));
+            w[m] = raw1_to_f32<QT>(element(wr, m));
 #pragma unroll
         for (int m = 0; m < CK - 1; ++m)
-            win[m] = raw1_to_f32<QT>(load_raw1<QT>(p.conv_in, sbase + m));
+            win[m] = raw1_to_f32<QT>(element(winr, m));
+    }
+    __device__ __forceinline__ static uint32_t element(const uint32_t *words, int m)
+    {
+        if constexpr (ES == 4)
+            return words[m];
+        else
+            return (words[m / 2] >> (16 * (m % 2))) & 0xffffu;
     }
     __device__ __forceinline__ float tap(float x)
     {
@@ -212,13 +239,22 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     __shared__ float sc_s[GS ? kTokGroup : 1][5];
     constexpr int GT = (kTokGroup + NW - 1) / NW;  // group tokens per wave
 
+    // One field from each 64-byte line of the kernel arguments, consumed together:
+    // the four lines are fetched at once behind one wait, instead of line by line
+    // as each field is first used, a memory round trip each.
+    asm volatile("" ::"s"(p.in.q), "s"(p.in.decay_param), "s"(p.hc.Hv), "s"(p.T));
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv;
     const int h = blockIdx.x % Hv;
     const int b = blockIdx.x / Hv;
-    const int slot = p.slots ? p.slots[b] : b;
-    if (slot < 0 || slot >= p.num_slots)
-        return;  // whole workgroup leaves before any barrier
+    // A sentinel or out-of-range slot: the workgroup issues its loads from slot 0
+    // (in bounds: the host launches nothing when there are no slots) and leaves
+    // once they are issued, before any barrier or store. Leaving here instead
+    // would put a wait for the slot and the kernel arguments behind the branch
+    // in front of every load.
+    const int slot_arg = p.slots ? p.slots[b] : b;
+    const bool live = slot_arg >= 0 && slot_arg < p.num_slots;
+    const int slot = live ? slot_arg : 0;
     const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -228,11 +264,13 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     const int row0 = wave * RPW + sub;
     const int vrow = wave * RPW + (lane % RPW);  // the v element this lane fetches
 
-    float dec_rate = 0.f, dtb = 0.f;
+    // per-head gate parameters: vector loads issued with the token's inputs (ahead
+    // of the state in the in-order return queue); exp is taken where they are used
+    float dparam = 0.f, dtb = 0.f;
     if (flags & F_RAW_GATES) {
-        const float dp = p.in.decay_param[h];
-        dec_rate = hc.decay_kind == 0 ? -expf(dp) : dp;
-        dtb = p.in.dt_bias[h];
+        const int hz = h + vgpr_zero();
+        dparam = p.in.decay_param[hz];
+        dtb = p.in.dt_bias[hz];
     }
 
     // Token 0's activations are issued before the state: vector-memory returns
@@ -251,16 +289,21 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
 #pragma unroll
         for (int i = 0; i < GT; ++i) {
             const int64_t r = (int64_t)b * p.T + t0 + min(wave + i * NW, tn - 1);
-            gwa[i] = load_gate(gsa, r * Hv + h, gdt0);
-            gwb[i] = load_gate(gsb, r * Hv + h, gdt0);
+            const int64_t gi = r * Hv + h + vgpr_zero();
+            gwa[i] = load_gate(gsa, gi, gdt0);
+            gwb[i] = load_gate(gsb, gi, gdt0);
         }
     };
     if constexpr (GS)
         load_group_gates(0, min(p.T, kTokGroup));
     else
         load_token<DK, DV, QT, PPR, LPR, CK == 0>(tr, p, (int64_t)b * p.T, h, kh, col, vrow);
-    // fused conv: this thread's channel (q, k or v), its raw input of the first
-    // token group, weights and window, all issued before the state loads
+    // fused conv: this thread's channel (q, k or v) and its raw inputs of the first
+    // token group, issued before the state loads, and its taps and window: before
+    // the state too for one token per sequence (the conv then runs while the state
+    // is in flight), right after it for several (the multi-token kernel has no
+    // registers to spare across the state loads, nor has a 16-wave workgroup)
+    constexpr bool kTapsFirst = !GS && NW <= 8;
     const int64_t nch = 2 * (int64_t)hc.Hk * DK + (int64_t)Hv * DV;
     const int cl = threadIdx.x;  // channel within the workgroup's 2 dk + dv
     int64_t cch = 0;             // its index in the conv channel order
@@ -280,12 +323,13 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
             xsrc = p.in.v; xoff = (int64_t)h * DV + (cl - 2 * DK); xstride = p.in.v_stride;
         }
         if (cl < NCH) {
-            cvl.load(p, cch, ((int64_t)slot * nch + cch) * (CK - 1));
             const int tn = min(p.T, kTokGroup);
 #pragma unroll
             for (int tt = 0; tt < kTokGroup; ++tt)
                 if (tt < tn)
                     xr[tt] = load_raw1<QT>(xsrc, ((int64_t)b * p.T + tt) * xstride + xoff);
+            if constexpr (kTapsFirst)
+                cvl.load(p, cch, ((int64_t)slot * nch + cch) * (CK - 1));
         }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the token loads ahead of the state loads
@@ -295,6 +339,10 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         S[i] = load_state4(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR));
+    if constexpr (CK > 0 && !kTapsFirst) {
+        if (cl < NCH)
+            cvl.load(p, cch, ((int64_t)slot * nch + cch) * (CK - 1));
+    }
     // the gated norm's z and weights for the first token group, behind the state:
     // the epilogue then waits on nothing (branch-free: without the norm the loads
     // read the state's first word and are not used)
@@ -323,6 +371,8 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
         nw[m] = (gated ? p.in.norm_w : p.state)[gated && j < DV ? j : 0];
     }
     __builtin_amdgcn_sched_barrier(0);  // ... and their use behind the state loads
+    if (!live)
+        return;  // whole workgroup, before any barrier or store
     const bool raw_gates = flags & F_RAW_GATES;
 
     // fused conv of tokens [t0, t0 + tn) into y_s (xr holds their raw inputs)
@@ -353,6 +403,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     auto gates = [&](float ga, float gb, float &alpha, float &beta) {
         float g;
         if (raw_gates) {
+            const float dec_rate = hc.decay_kind == 0 ? -expf(dparam) : dparam;
             g = dec_rate * softplus_f(ga + dtb);
             beta = sigmoid_f(gb);
         } else {
@@ -413,6 +464,8 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
         }
     };
     if constexpr (CK > 0) {
+        if (cl < NCH)
+            cvl.convert();
         conv_group(min(p.T, kTokGroup));
         __syncthreads();
         if constexpr (GS) {
@@ -593,7 +646,7 @@ bool decode_supported(int dk, int dv)
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
 {
-    if (p.B == 0)
+    if (p.B == 0 || p.num_slots == 0)  // no slots: every sequence is a sentinel
         return hipSuccess;
     const int dk = p.hc.dk, dv = p.hc.dv;
     if (dk == 128 && dv == 128)

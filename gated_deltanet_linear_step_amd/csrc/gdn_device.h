@@ -91,6 +91,17 @@ __device__ __forceinline__ float4 load_act4_t(const void *p, int64_t idx)
 // holding it is loaded (the base pointer is 4-byte aligned -- the host checks),
 // then the conversion is selected. Split into the load and the conversion so a
 // caller can issue other loads in between.
+// A zero the compiler cannot see through, in a VGPR. Added to a workgroup-uniform
+// element index it keeps that load on the vector memory path: as a scalar load it
+// would need its own wait, which also holds back every vector load whose address
+// comes from a scalar register loaded at the same time.
+__device__ __forceinline__ int vgpr_zero()
+{
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
 __device__ __forceinline__ uint32_t load_word_nb(const void *p, int64_t idx, int dt)
 {
     const int64_t byte = dt == DT_F32 ? idx * 4 : idx * 2;
