@@ -37,6 +37,10 @@
 //    are computed once per conv group, by one wave per token, and shared through
 //    LDS instead of by every lane for every token. The operations are the
 //    single-token path's, so a call and any split of it agree bit for bit.
+//  * One token per sequence (the serving step): a kernel of its own, with no
+//    token loop, so its registers fit easily; each wave forms the gated norm's
+//    sum of squares over all rows (in the order the multi-token epilogue uses,
+//    so results agree bit for bit) and stores its own rows' outputs.
 
 #include "gdn_device.h"
 #include "gdn_kernels.h"
@@ -207,21 +211,29 @@ constexpr int decode_lpr()
     return DK == 128 ? GDN_DECODE_LPR128 : DK == 256 ? GDN_DECODE_LPR256 : DK == 96 ? 8 : DK / 4;
 }
 
-// Two 8-wave workgroups per CU (4 waves per SIMD, 128 VGPRs) for the shapes whose
-// state share fits; the larger shapes take the registers they need.
+// GS (fused layer, several tokens per sequence): the per-token scalars (q/k norms,
+// k.q, gates) are computed once per token of a conv group and shared through LDS,
+// instead of by every lane for every token. The arithmetic is the per-lane one,
+// operation for operation, so a call and any split of it agree bit for bit.
+// Token modes: MODE_ANY (one or more tokens, per-lane scalars), MODE_GROUP (fused
+// layer, several tokens: scalars once per conv group), MODE_ONE (one token per
+// sequence: no token loop, and each wave stores its own rows' outputs).
+enum { MODE_ANY = 0, MODE_GROUP = 1, MODE_ONE = 2 };
+
+// Two 8-wave workgroups per CU (4 waves per SIMD, at most 128 VGPRs) for the shapes
+// whose state share fits; the larger shapes take the registers they need. The
+// one-token kernel needs about 87 VGPRs; held to 80 for a third workgroup per CU
+// it spills 28 bytes per lane and runs 13 % slower.
 template <int DK, int DV, int NW>
 constexpr int decode_min_waves()
 {
     return NW == 8 && DK * DV <= 128 * 128 ? 4 : (NW == 6 ? 3 : 1);
 }
 
-// GS (fused layer, several tokens per sequence): the per-token scalars (q/k norms,
-// k.q, gates) are computed once per token of a conv group and shared through LDS,
-// instead of by every lane for every token. The arithmetic is the per-lane one,
-// operation for operation, so a call and any split of it agree bit for bit.
-template <int DK, int DV, int NW, int QT, int CK, bool GS>
+template <int DK, int DV, int NW, int QT, int CK, int MODE>
 __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void decode_kernel(DecodeParams p)
 {
+    constexpr bool GS = MODE == MODE_GROUP;
     constexpr int LPR = decode_lpr<DK, DV>();  // lanes holding one row
     constexpr int PPR = DK / (4 * LPR);        // float4 pieces of a row per lane
     constexpr int RPI = 64 / LPR;              // rows per wave-wide load
@@ -348,10 +360,19 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     // read the state's first word and are not used)
     constexpr int ZT = (kTokGroup + NW - 1) / NW, ZJ = (DV + 63) / 64;
     const bool gated = flags & F_GATED_NORM;
+    // One token per sequence: every wave stores the outputs of its own rows (lane
+    // < RPW holds row wave RPW + lane), instead of one wave storing them all.
+    constexpr bool solo = MODE == MODE_ONE;
+    const int jsolo = wave * RPW + (lane % RPW);
     uint32_t zw[ZT][ZJ];
     float nw[ZJ];
     auto prefetch_z = [&](int t0, int tn) {
         const void *zsrc = gated ? p.in.z : static_cast<const void *>(p.state);
+        if constexpr (solo) {
+            const int64_t obase = ((int64_t)b * Hv + h) * DV;
+            zw[0][0] = load_word_nb(zsrc, gated ? obase + jsolo : 0, p.in.z_dt);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < ZT; ++i) {
             const int tt = wave + i * NW;
@@ -367,7 +388,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     prefetch_z(0, min(p.T, kTokGroup));
 #pragma unroll
     for (int m = 0; m < ZJ; ++m) {
-        const int j = lane + 64 * m;
+        const int j = solo ? jsolo : lane + 64 * m;
         nw[m] = (gated ? p.in.norm_w : p.state)[gated && j < DV ? j : 0];
     }
     __builtin_amdgcn_sched_barrier(0);  // ... and their use behind the state loads
@@ -529,9 +550,27 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
         }
     };
 
+    float zsilu = 0.f;  // solo: SiLU(z) of this lane's row, formed before the last barrier
     // Gated RMS norm (or plain copy) of the tokens [t0, t0 + tn): one wave per token.
     // (z and the norm weights come from the registers prefetch_z filled)
     auto epilogue = [&](int t0, int tn) {
+        if constexpr (solo) {
+            // every wave forms the same sum of squares, in the order the
+            // one-wave-per-token epilogue below uses, so both agree bit for bit
+            const int64_t obase = ((int64_t)b * Hv + h) * DV;
+            if (gated) {
+                float ss = 0.f;
+                for (int j = lane; j < DV; j += 64)
+                    ss = fmaf(o_s[0][j], o_s[0][j], ss);
+                ss = group_sum<64>(ss);
+                const float inv = rsqrtf(ss / (float)DV + hc.norm_eps);
+                if (lane < RPW)
+                    store_act(p.out, obase + jsolo, p.out_dt, o_s[0][jsolo] * inv * nw[0] * zsilu);
+            } else if (lane < RPW) {
+                store_act(p.out, obase + jsolo, p.out_dt, o_s[0][jsolo]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < ZT; ++i) {
             const int tt = wave + i * NW;
@@ -562,7 +601,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
 
     // token 0 in straight-line code, so each row piece is used as soon as it lands
     process_token(0, (int64_t)b * p.T);
-    for (int t = 1; t < p.T; ++t) {
+    for (int t = 1; t < (solo ? 1 : p.T); ++t) {
         const int tt = t % kTokGroup;
         if (tt == 0) {  // o_s (and y_s) hold a full group: drain it, convolve the next
             load_group(t, min(p.T - t, kTokGroup));
@@ -590,32 +629,33 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
         if (cl < NCH && (cl >= 2 * DK || qk_writer))
             cvl.store(p, ((int64_t)slot * nch + cch) * (CK - 1));
     }
+    if (solo && gated)
+        zsilu = silu_f(word_to_f32(zw[0][0], ((int64_t)b * Hv + h) * DV + jsolo, p.in.z_dt));
     __syncthreads();
     const int tlast0 = ((p.T - 1) / kTokGroup) * kTokGroup;
     epilogue(tlast0, p.T - tlast0);
 }
 
-template <int DK, int DV, int NW, int CK, bool GS>
-void launch_decode_gs(const DecodeParams &p, hipStream_t s)
+template <int DK, int DV, int NW, int CK, int MODE>
+void launch_decode_mode(const DecodeParams &p, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)p.B * p.hc.Hv)), block(NW * 64);
     switch (p.in.qkv_dt) {
-    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK, GS>), grid, block, 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK, GS>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK, GS>), grid, block, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK, MODE>), grid, block, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK, MODE>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK, MODE>), grid, block, 0, s, p); break;
     }
 }
 
 template <int DK, int DV, int NW, int CK>
 void launch_decode_ck(const DecodeParams &p, hipStream_t s)
 {
-    if constexpr (CK > 0) {
-        if (p.T > 1) {
-            launch_decode_gs<DK, DV, NW, CK, true>(p, s);
-            return;
-        }
-    }
-    launch_decode_gs<DK, DV, NW, CK, false>(p, s);
+    if (p.T == 1)
+        launch_decode_mode<DK, DV, NW, CK, MODE_ONE>(p, s);
+    else if constexpr (CK > 0)
+        launch_decode_mode<DK, DV, NW, CK, MODE_GROUP>(p, s);
+    else
+        launch_decode_mode<DK, DV, NW, CK, MODE_ANY>(p, s);
 }
 
 template <int DK, int DV, int NW>
