@@ -500,21 +500,27 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     // o_s[tt] for the group epilogue.
     auto process_token = [&](int tt, int64_t r) {
         float4 kk[PPR], qq[PPR];
-        float vv, alpha, beta, kq;
+        float vr[RPL];  // v of each of the lane's rows
+        float alpha, beta, kq;
         if constexpr (CK > 0) {
 #pragma unroll
             for (int m = 0; m < PPR; ++m) {
                 qq[m] = *reinterpret_cast<const float4 *>(&y_s[tt][col + 4 * LPR * m]);
                 kk[m] = *reinterpret_cast<const float4 *>(&y_s[tt][DK + col + 4 * LPR * m]);
             }
-            vv = y_s[tt][2 * DK + vrow];
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+                vr[rr] = y_s[tt][2 * DK + row0 + rr * RPI];
         } else {
 #pragma unroll
             for (int m = 0; m < PPR; ++m) {
                 kk[m] = raw4_to_f32<QT>(tr.k[m]);
                 qq[m] = raw4_to_f32<QT>(tr.q[m]);
             }
-            vv = raw1_to_f32<QT>(tr.v);
+            const float vv = raw1_to_f32<QT>(tr.v);  // row vrow's v, spread to the rows
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+                vr[rr] = __shfl(vv, sub + rr * RPI, 64);
         }
         if constexpr (GS) {
             const float ik = sc_s[tt][0], iq = sc_s[tt][1];
@@ -535,8 +541,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
             float4 *Sr = &S[rr * PPR];
             const float pk = group_sum<LPR>(dotn<PPR>(Sr, kk));
             const float pq = group_sum<LPR>(dotn<PPR>(Sr, qq));
-            const float vj = __shfl(vv, sub + rr * RPI, 64);
-            const float d = beta * fmaf(-alpha, pk, vj);
+            const float d = beta * fmaf(-alpha, pk, vr[rr]);
             const float o = hc.scale * fmaf(alpha, pq, d * kq);
 #pragma unroll
             for (int m = 0; m < PPR; ++m) {
