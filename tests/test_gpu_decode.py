@@ -204,7 +204,8 @@ def test_activation_and_output_dtypes(act, out_dtype, T):
 
 
 def test_state_slots_and_out_of_range_slot():
-    B, Hk, Hv, d = 4, 2, 4, 64
+    # slot 99 is past the pool and -1 is a sentinel: neither sequence touches memory
+    B, Hk, Hv, d = 5, 2, 4, 64
     rng = np.random.default_rng(21)
     q = torch.from_numpy(rng.normal(size=(B, Hk, d)).astype(np.float32)).to(DEV)
     k = torch.from_numpy(rng.normal(size=(B, Hk, d)).astype(np.float32)).to(DEV)
@@ -212,14 +213,15 @@ def test_state_slots_and_out_of_range_slot():
     g = torch.full((B, Hv), -0.1, device=DEV)
     beta = torch.full((B, Hv), 0.5, device=DEV)
     pool = torch.from_numpy(rng.normal(0, 0.1, size=(6, Hv, d, d)).astype(np.float32)).to(DEV)
-    slots = torch.tensor([5, 0, 99, 2], dtype=torch.int32, device=DEV)
+    slot_list = [5, 0, 99, 2, -1]
+    slots = torch.tensor(slot_list, dtype=torch.int32, device=DEV)
     before = pool.clone()
     out = torch.full((B, Hv, d), 7.0, device=DEV)
     ops.decode_step(q, k, v, pool, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=B,
                     g=g, beta=beta, state_slots=slots, out=out)
     torch.cuda.synchronize()
-    for bi, s in enumerate([5, 0, 99, 2]):
-        if s >= pool.shape[0]:
+    for bi, s in enumerate(slot_list):
+        if s < 0 or s >= pool.shape[0]:
             assert torch.all(out[bi] == 7.0)
             continue
         yo, So = oracle.core(f64(q[bi:bi + 1]), f64(k[bi:bi + 1]), f64(v[bi:bi + 1]),

@@ -113,9 +113,9 @@ def test_fused_layer_dtypes(act, out_dtype):
 
 
 def test_fused_layer_slots_and_out_of_range_slot():
-    B, Hk, Hv, d, nslots = 3, 2, 4, 64, 5
+    B, Hk, Hv, d, nslots = 4, 2, 4, 64, 5
     W = to_dev(synth.decode_batch(seed=61, B=nslots, Hk=Hk, Hv=Hv, dk=d, dv=d))
-    slots = [4, 77, 1]
+    slots = [4, 77, 1, -1]  # 77: past the pool; -1: a sentinel
     # activations of the three sequences; states and conv windows live in a pool of 5
     x = W["x_d"][:B].contiguous()
     z, a, b = W["z_d"][:B].contiguous(), W["a_d"][:B].contiguous(), W["b_d"][:B].contiguous()
@@ -126,7 +126,7 @@ def test_fused_layer_slots_and_out_of_range_slot():
               slots=torch.tensor(slots, dtype=torch.int32, device=DEV), out=out)
     torch.cuda.synchronize()
     for bi, s in enumerate(slots):
-        if s >= nslots:
+        if s < 0 or s >= nslots:
             assert torch.all(out[bi] == 7.0)
             continue
         Wi = dict(W)
