@@ -23,10 +23,14 @@
 //        p_j = a (S_j.k),  o_j = scale (a (S_j.q) + d_j (k.q)),
 //    which is S_new.q expanded -- the same value in another rounding order (the
 //    ferrox-core page notes this expansion next to its throughput probe).
-//  * a token's activations are loaded before anything that waits on them; v
-//    arrives one element per lane and is spread to the rows by shuffles. The
-//    outputs are gathered in LDS and the gated RMS norm runs over them after
-//    each group of tokens.
+//  * a token's activations are loaded before anything that waits on them, and
+//    nothing waits on memory before the state loads are issued (kernel
+//    arguments fetched in one round trip, gate words as vector loads, the conv
+//    taps and window kept as raw words until after the state loads). In the
+//    unfused step v arrives one element per lane and is spread to the rows by
+//    shuffles; in the fused layer each lane reads its rows' v from the conv
+//    output in LDS. The outputs are gathered in LDS and the gated RMS norm runs
+//    over them after each group of tokens.
 //  * CK > 0 (gdn_decode_layer): q, k, v arrive before the causal conv. Thread c
 //    of the workgroup owns one of the 2 dk + dv channels it reads (its weights
 //    and the window of the last CK-1 raw inputs in registers), convolves a group
@@ -194,9 +198,9 @@ __device__ __forceinline__ float dotn(const float4 *a, const float4 *b)
 
 // Lanes per state row: 16 for the 128-wide rows (two float4 pieces per lane, the
 // row sums stay within a 16-lane DPP row), dk/4 (one piece per lane) otherwise.
-// At 128 x 128, 16 lanes per row take about a sixth of the reduction steps of 32
-// (4 rows per lane with 2 x 4 DPP steps each, against 8 rows with 2 x 5 steps, one
-// of them through LDS) for 8 more VGPRs of k and q; 32 and 8 lanes spill.
+// At 128 x 128, 16 lanes per row take 40 % of the reduction steps of 32 (4 rows
+// per lane with 2 x 4 DPP steps each, against 8 rows with 2 x 5 steps, one of
+// them through LDS) for 8 more VGPRs of k and q; 32 and 8 lanes spill.
 #ifndef GDN_DECODE_LPR128
 #define GDN_DECODE_LPR128 16
 #endif
@@ -211,19 +215,18 @@ constexpr int decode_lpr()
     return DK == 128 ? GDN_DECODE_LPR128 : DK == 256 ? GDN_DECODE_LPR256 : DK == 96 ? 8 : DK / 4;
 }
 
-// GS (fused layer, several tokens per sequence): the per-token scalars (q/k norms,
-// k.q, gates) are computed once per token of a conv group and shared through LDS,
-// instead of by every lane for every token. The arithmetic is the per-lane one,
-// operation for operation, so a call and any split of it agree bit for bit.
 // Token modes: MODE_ANY (one or more tokens, per-lane scalars), MODE_GROUP (fused
-// layer, several tokens: scalars once per conv group), MODE_ONE (one token per
-// sequence: no token loop, and each wave stores its own rows' outputs).
+// layer, several tokens: the per-token scalars -- q/k norms, k.q, gates -- once per
+// token of a conv group, shared through LDS), MODE_ONE (one token per sequence: no
+// token loop, and each wave stores its own rows' outputs). The arithmetic is the
+// same operation for operation in every mode, so a call and any split of it agree
+// bit for bit.
 enum { MODE_ANY = 0, MODE_GROUP = 1, MODE_ONE = 2 };
 
 // Two 8-wave workgroups per CU (4 waves per SIMD, at most 128 VGPRs) for the shapes
 // whose state share fits; the larger shapes take the registers they need. The
-// one-token kernel needs about 87 VGPRs; held to 80 for a third workgroup per CU
-// it spills 28 bytes per lane and runs 13 % slower.
+// one-token kernel needs about 85 VGPRs; held to 80 for a third workgroup per CU
+// it spills 16-28 bytes per lane and runs 6-13 % slower.
 template <int DK, int DV, int NW>
 constexpr int decode_min_waves()
 {
