@@ -89,11 +89,17 @@ def decode_bench(args, torch, ops, synth):
         kw = dict(Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
                   decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"])
         x = S["x"]
-        # layer[j]: conv state read from buffer j, written to the other one
+        # layer[j]: conv state read from buffer j, written to the other one;
+        # layer_stream: the same calls with GDN_STREAM_STATE (for the rotating sets,
+        # whose 537 MB of state does not stay in the 256 MB Infinity Cache)
+        pairs = ((S["conv_state"], S["conv_b"]), (S["conv_b"], S["conv_state"]))
         S["layer"] = [ops.prepare_decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
                                                S["state"], S["conv_w"], cin, cout, S["out"], **kw)
-                      for cin, cout in ((S["conv_state"], S["conv_b"]),
-                                        (S["conv_b"], S["conv_state"]))]
+                      for cin, cout in pairs]
+        S["layer_stream"] = [ops.prepare_decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
+                                                      S["state"], S["conv_w"], cin, cout,
+                                                      S["out"], stream_state=True, **kw)
+                             for cin, cout in pairs]
         S["parity"] = 0
         S["conv"] = ops.prepare_conv_update(S["x"], S["conv_w"], S["conv_state"], S["y"])
         y = S["y"]
@@ -102,8 +108,8 @@ def decode_bench(args, torch, ops, synth):
         sets.append(S)
     main = sets[0]
 
-    def step(S):
-        S["layer"][S["parity"]].launch()
+    def step(S, key="layer"):
+        S[key][S["parity"]].launch()
         S["parity"] ^= 1
 
     def timed(fn, n):
@@ -146,12 +152,17 @@ def decode_bench(args, torch, ops, synth):
     dec_bytes = state_bytes + act_bytes
     value = state_bytes / (ms_step * 1e-3) / 1e9
 
-    # rotating variant: 4 state sets, > Infinity Cache
+    # rotating variant: 4 state sets, > Infinity Cache; with GDN_STREAM_STATE (the
+    # caller's hint for exactly this case), then without it
+    for _ in range(nsets * 4):
+        for S in sets:
+            step(S, "layer_stream")
+    Kr = max(nsets, (K // nsets) * nsets)
+    ms_rot, _ = timed(lambda i: step(sets[i % nsets], "layer_stream"), Kr)
     for _ in range(nsets * 4):
         for S in sets:
             step(S)
-    Kr = max(nsets, (K // nsets) * nsets)
-    ms_rot, _ = timed(lambda i: step(sets[i % nsets]), Kr)
+    ms_rot_plain, _ = timed(lambda i: step(sets[i % nsets]), Kr)
 
     src_hash = kernel_source_hash(["gdn_decode.hip", "gdn_device.h", "gdn_kernels.h"])
     traffic = read_traffic("decode_layer_b64_bf16_traffic.md", src_hash)
@@ -166,8 +177,10 @@ def decode_bench(args, torch, ops, synth):
         two_launch=dict(step="gdn_conv_update + gdn_decode_step", ms_per_step=ms_two,
                         value=state_bytes / (ms_two * 1e-3) / 1e9, unit="GB/s"),
         rotating=dict(sets=nsets, footprint_mb=nsets * (state_bytes // 2) / 1e6,
-                      ms_per_step=ms_rot,
-                      value=state_bytes / (ms_rot * 1e-3) / 1e9, unit="GB/s"),
+                      stream_state=True, ms_per_step=ms_rot,
+                      value=state_bytes / (ms_rot * 1e-3) / 1e9, unit="GB/s",
+                      ms_per_step_no_hint=ms_rot_plain,
+                      value_no_hint=state_bytes / (ms_rot_plain * 1e-3) / 1e9),
         config=dict(workload="batched decode: B=64 x 1 token, Hk=16, Hv=32, dk=dv=128, tiled map, "
                              "bf16 N(0,1) activations, fp32 state N(0,0.02^2), conv K=4",
                     batch=B, tokens_per_seq=1, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map="tiled",
@@ -265,12 +278,15 @@ def deep_model_bench(torch, ops, synth, batches=(1, 32), layers=48, steps=(100, 
     token, each with its own seeded taps, gates, norm, state and conv window (seed
     4*1000 + layer); one token step = `layers` gdn_decode_layer launches. Timed
     uncaptured and as one captured HIP graph (two token steps per graph, so the conv
-    windows alternate back to their first buffers)."""
+    windows alternate back to their first buffers). When the stack's states exceed the
+    256 MB Infinity Cache (B=32: 4.8 GB; B=1: 151 MB does not), the calls carry
+    GDN_STREAM_STATE, as a caller of such a stack would set it."""
     dev = torch.device("cuda:0")
     Hk, Hv, d = 16, 48, 128
     QK = Hk * d
     res = {}
     for B, nsteps in zip(batches, steps):
+        stream_state = layers * B * Hv * d * d * 4 > 256 * 2**20
         cap = torch.cuda.Stream()
         Ls = []
         for layer in range(layers):
@@ -282,7 +298,7 @@ def deep_model_bench(torch, ops, synth, batches=(1, 32), layers=48, steps=(100, 
             x = S["x"]
             kw = dict(Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=B, a=S["a"],
                       b=S["b"], decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"],
-                      norm_weight=S["norm_w"])
+                      norm_weight=S["norm_w"], stream_state=stream_state)
             pairs = ((S["conv_state"], S["cb"]), (S["cb"], S["conv_state"]))
             S["eager"] = [ops.prepare_decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:],
                                                    S["state"], S["conv_w"], ci, co, S["out"],
@@ -329,7 +345,7 @@ def deep_model_bench(torch, ops, synth, batches=(1, 32), layers=48, steps=(100, 
         res[f"B{B}"] = dict(ms_per_token_step=ms_eager, ms_per_token_step_graph=ms_graph,
                             state_GBps=state_bytes / (ms_eager * 1e-3) / 1e9,
                             state_GBps_graph=state_bytes / (ms_graph * 1e-3) / 1e9,
-                            state_bytes_per_step=state_bytes)
+                            state_bytes_per_step=state_bytes, stream_state=stream_state)
         del graph, Ls
         torch.cuda.empty_cache()
     return dict(workload=f"deep-model decode: {layers} layers x gdn_decode_layer per token, "

@@ -16,7 +16,8 @@
 
 namespace {
 
-constexpr uint32_t kKnownFlags = GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM;
+constexpr uint32_t kPrefillFlags = GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM;
+constexpr uint32_t kDecodeFlags = kPrefillFlags | GDN_STREAM_STATE;
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
 
 bool dtype_ok(int32_t dt) { return dt == GDN_F32 || dt == GDN_F16 || dt == GDN_BF16; }
@@ -31,7 +32,7 @@ bool aligned(const void *p, int64_t bytes)
 // the flags require. On success fills the kernel-side copies.
 gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dtype,
                         const void *out, const float *state, bool (*supported)(int, int),
-                        gdn::HeadCfg &hc, gdn::ActInputs &ai)
+                        uint32_t known_flags, gdn::HeadCfg &hc, gdn::ActInputs &ai)
 {
     if (!d || !in || !out || !state)
         return GDN_ERR_NULL;
@@ -41,7 +42,7 @@ gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dty
         return GDN_ERR_SHAPE;
     if (d->head_map != GDN_MAP_GROUPED && d->head_map != GDN_MAP_TILED)
         return GDN_ERR_SHAPE;
-    if ((d->flags & ~kKnownFlags) != 0)
+    if ((d->flags & ~known_flags) != 0)
         return GDN_ERR_UNSUPPORTED;
     if (!supported(d->head_dim_k, d->head_dim_v))
         return GDN_ERR_UNSUPPORTED;
@@ -207,7 +208,8 @@ gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_p
                            int32_t num_slots, int32_t out_dtype, void *out, void *stream)
 {
     gdn::DecodeParams p{};
-    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::decode_supported, p.hc, p.in);
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::decode_supported, kDecodeFlags,
+                                 p.hc, p.in);
     if (st != GDN_OK)
         return st;
     if (batch < 0 || tokens_per_seq < 1 || num_slots < 0)
@@ -234,7 +236,8 @@ gdn_status gdn_decode_layer(const gdn_dims *dims, int32_t batch, int32_t tokens_
                             void *out, void *stream)
 {
     gdn::DecodeParams p{};
-    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::decode_supported, p.hc, p.in);
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::decode_supported, kDecodeFlags,
+                                 p.hc, p.in);
     if (st != GDN_OK)
         return st;
     if (!conv || !conv->weight || !conv->state_in || !conv->state_out)
@@ -294,7 +297,8 @@ gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
                                size_t workspace_bytes, void *stream)
 {
     gdn::PrefillParams p{};
-    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::prefill_supported, p.hc, p.in);
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::prefill_supported, kPrefillFlags,
+                                 p.hc, p.in);
     if (st != GDN_OK)
         return st;
     if (num_seqs < 0 || total_tokens < 0)

@@ -52,12 +52,6 @@
 #ifndef GDN_DECODE_NW
 #define GDN_DECODE_NW 8  // waves per workgroup for the 128 x 128 state
 #endif
-#ifndef GDN_NT_LOAD
-#define GDN_NT_LOAD 0  // 1: non-temporal state loads
-#endif
-#ifndef GDN_NT_STORE
-#define GDN_NT_STORE 0  // 1: non-temporal state stores
-#endif
 
 namespace gdn {
 namespace {
@@ -66,24 +60,30 @@ constexpr int kTokGroup = 8;  // tokens whose outputs are buffered in LDS at onc
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// State pieces, plain or with non-temporal hints (GDN_STREAM_STATE: states that do
+// not stay in the last-level cache between calls). At B=64 x 32 heads the plain
+// form is 10 % faster while the 128 MiB state stays in the Infinity Cache; on
+// streams past it (four rotating state sets, 48 layers at B=32) the hinted form is
+// 11 % faster. Hinting only the stores changes neither.
+template <bool NT>
 __device__ __forceinline__ float4 load_state4(const float *p)
 {
-#if GDN_NT_LOAD
-    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-#else
-    f32x4 v = *reinterpret_cast<const f32x4 *>(p);
-#endif
+    f32x4 v;
+    if constexpr (NT)
+        v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    else
+        v = *reinterpret_cast<const f32x4 *>(p);
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+template <bool NT>
 __device__ __forceinline__ void store_state4(float *p, float4 s)
 {
     f32x4 v = {s.x, s.y, s.z, s.w};
-#if GDN_NT_STORE
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
-#else
-    *reinterpret_cast<f32x4 *>(p) = v;
-#endif
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+    else
+        *reinterpret_cast<f32x4 *>(p) = v;
 }
 
 // Activations of one token for one wave, as raw bits: the k and q pieces, the
@@ -233,7 +233,7 @@ constexpr int decode_min_waves()
     return NW == 8 && DK * DV <= 128 * 128 ? 4 : (NW == 6 ? 3 : 1);
 }
 
-template <int DK, int DV, int NW, int QT, int CK, int MODE>
+template <int DK, int DV, int NW, int QT, int CK, int MODE, bool NT>
 __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void decode_kernel(DecodeParams p)
 {
     constexpr bool GS = MODE == MODE_GROUP;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     float4 S[NI];  // S[r * PPR + m]: piece m of the lane's row r
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-        S[i] = load_state4(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR));
+        S[i] = load_state4<NT>(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR));
     if constexpr (CK > 0 && !kTapsFirst) {
         if (cl < NCH)
             cvl.load(p, cch, ((int64_t)slot * nch + cch) * (CK - 1));
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-        store_state4(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR), S[i]);
+        store_state4<NT>(Sg + (row0 + (i / PPR) * RPI) * DK + col + 4 * LPR * (i % PPR), S[i]);
     if constexpr (CK > 0) {
         // the window after this call's tokens; q/k channels from one v-head per k-head
         const bool qk_writer = hc.head_map == 0 ? (h % (Hv / hc.Hk) == 0) : (h < hc.Hk);
@@ -644,15 +644,24 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
     epilogue(tlast0, p.T - tlast0);
 }
 
-template <int DK, int DV, int NW, int CK, int MODE>
-void launch_decode_mode(const DecodeParams &p, hipStream_t s)
+template <int DK, int DV, int NW, int CK, int MODE, bool NT>
+void launch_decode_nt(const DecodeParams &p, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)p.B * p.hc.Hv)), block(NW * 64);
     switch (p.in.qkv_dt) {
-    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK, MODE>), grid, block, 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK, MODE>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK, MODE>), grid, block, 0, s, p); break;
+    case DT_F32: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F32, CK, MODE, NT>), grid, block, 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_F16, CK, MODE, NT>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<DK, DV, NW, DT_BF16, CK, MODE, NT>), grid, block, 0, s, p); break;
     }
+}
+
+template <int DK, int DV, int NW, int CK, int MODE>
+void launch_decode_mode(const DecodeParams &p, hipStream_t s)
+{
+    if (p.hc.flags & F_STREAM_STATE)
+        launch_decode_nt<DK, DV, NW, CK, MODE, true>(p, s);
+    else
+        launch_decode_nt<DK, DV, NW, CK, MODE, false>(p, s);
 }
 
 template <int DK, int DV, int NW, int CK>

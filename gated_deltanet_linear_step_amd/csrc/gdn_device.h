@@ -8,7 +8,7 @@
 namespace gdn {
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum : uint32_t { F_L2NORM = 1u, F_RAW_GATES = 2u, F_GATED_NORM = 4u };
+enum : uint32_t { F_L2NORM = 1u, F_RAW_GATES = 2u, F_GATED_NORM = 4u, F_STREAM_STATE = 8u };
 
 // ---- 16-bit float conversions (round to nearest even) ------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
 F32, F16, BF16 = 0, 1, 2
 MAP_GROUPED, MAP_TILED = 0, 1
 DECAY_LOG_RATE, DECAY_NEGATIVE_RATE = 0, 1
-L2NORM_QK, RAW_GATES, GATED_NORM = 1, 2, 4
+L2NORM_QK, RAW_GATES, GATED_NORM, STREAM_STATE = 1, 2, 4, 8
 CHUNK = 64
 
 EXPORTED = ["gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
@@ -213,11 +213,13 @@ def conv_update(x, weight, conv_state, *, cu_seqlens=None, num_seqs=None, y=None
 def decode_step(q, k, v, state, *, Hk, Hv, dk, dv, head_map, batch, tokens_per_seq=1,
                 a=None, b=None, decay_param=None, dt_bias=None, g=None, beta=None, z=None,
                 norm_weight=None, l2norm_qk=True, decay=DECAY_LOG_RATE, scale=0.0,
-                state_slots=None, out=None, out_dtype=torch.float32, stream=None):
+                state_slots=None, out=None, out_dtype=torch.float32, stream_state=False,
+                stream=None):
     """One call of gdn_decode_step. q, k [B*T][Hk*dk] (views allowed), v [B*T][Hv*dv],
-    state [slots][Hv][dv][dk] f32 updated in place. Returns out [B*T][Hv][dv]."""
+    state [slots][Hv][dv][dk] f32 updated in place. Returns out [B*T][Hv][dv].
+    stream_state sets GDN_STREAM_STATE (non-temporal state loads and stores)."""
     flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
-        (GATED_NORM if z is not None else 0)
+        (GATED_NORM if z is not None else 0) | (STREAM_STATE if stream_state else 0)
     dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
@@ -240,13 +242,14 @@ def decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_out, *, 
                  head_map, batch, tokens_per_seq=1, a=None, b=None, decay_param=None,
                  dt_bias=None, g=None, beta=None, z=None, norm_weight=None, l2norm_qk=True,
                  decay=DECAY_LOG_RATE, scale=0.0, state_slots=None, out=None,
-                 out_dtype=torch.float32, stream=None):
+                 out_dtype=torch.float32, stream_state=False, stream=None):
     """One call of gdn_decode_layer: q, k, v are the pre-conv projections (views of
     the mixed row allowed); conv_weight [channels][4], conv states [slots][channels][3]
     in q's dtype (read from conv_state_in, the new window written to conv_state_out);
-    state [slots][Hv][dv][dk] f32 updated in place. Returns out [B*T][Hv][dv]."""
+    state [slots][Hv][dv][dk] f32 updated in place. Returns out [B*T][Hv][dv].
+    stream_state sets GDN_STREAM_STATE (non-temporal state loads and stores)."""
     flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
-        (GATED_NORM if z is not None else 0)
+        (GATED_NORM if z is not None else 0) | (STREAM_STATE if stream_state else 0)
     dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
@@ -334,9 +337,9 @@ def prepare_decode_step(q, k, v, state, out, *, Hk, Hv, dk, dv, head_map, batch,
                         tokens_per_seq=1, a=None, b=None, decay_param=None, dt_bias=None,
                         g=None, beta=None, z=None, norm_weight=None, l2norm_qk=True,
                         decay=DECAY_LOG_RATE, scale=0.0, state_slots=None,
-                        stream=None) -> PreparedCall:
+                        stream_state=False, stream=None) -> PreparedCall:
     flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
-        (GATED_NORM if z is not None else 0)
+        (GATED_NORM if z is not None else 0) | (STREAM_STATE if stream_state else 0)
     dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
@@ -351,9 +354,9 @@ def prepare_decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_
                          Hv, dk, dv, head_map, batch, tokens_per_seq=1, a=None, b=None,
                          decay_param=None, dt_bias=None, g=None, beta=None, z=None,
                          norm_weight=None, l2norm_qk=True, decay=DECAY_LOG_RATE, scale=0.0,
-                         state_slots=None, stream=None) -> PreparedCall:
+                         state_slots=None, stream_state=False, stream=None) -> PreparedCall:
     flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
-        (GATED_NORM if z is not None else 0)
+        (GATED_NORM if z is not None else 0) | (STREAM_STATE if stream_state else 0)
     dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,

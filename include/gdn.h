@@ -75,7 +75,14 @@ enum {
     /* output y = o * (mean_j o_j^2 + norm_eps)^(-1/2) * norm_weight * silu(z)
      * over the dv values of each (token, v-head) (that page's `cpu_segment`
      * output section). Without it the output is the core o itself. */
-    GDN_GATED_NORM = 4u
+    GDN_GATED_NORM = 4u,
+    /* Decode entry points only (the prefill returns UNSUPPORTED): a cache hint
+     * for callers whose states do not stay in the GPU's last-level cache from
+     * one call to the next (many layers or sequences, more state than the
+     * cache holds). The state is loaded and stored with non-temporal hints;
+     * results are bit for bit those of a call without the flag. On states the
+     * cache does keep, the flag makes the step slower. */
+    GDN_STREAM_STATE = 8u
 };
 
 typedef struct gdn_dims {
@@ -88,7 +95,8 @@ typedef struct gdn_dims {
                             chunked prefill (128,128). Others: UNSUPPORTED. */
     int32_t head_map;    /* gdn_head_map */
     int32_t decay;       /* gdn_decay, used with GDN_RAW_GATES */
-    uint32_t flags;      /* GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM */
+    uint32_t flags;      /* GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM |
+                            GDN_STREAM_STATE */
     float scale;         /* read-out scale; 0 selects 1/sqrt(dk) */
     float l2_eps;        /* 0 selects 1e-6 */
     float norm_eps;      /* 0 selects 1e-6 */

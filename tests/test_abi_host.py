@@ -85,7 +85,7 @@ def test_decode_validation():
     assert decode(d=dims(dk=96, dv=128)) == UNSUPPORTED     # not built
     assert decode(d=dims(dk=256, dv=256)) == UNSUPPORTED
     assert decode(d=dims(dk=128, dv=32)) == UNSUPPORTED
-    assert decode(d=dims(flags=8)) == UNSUPPORTED           # unknown flag bit
+    assert decode(d=dims(flags=16)) == UNSUPPORTED          # unknown flag bit
     assert decode(d=dims(head_map=2)) == SHAPE
     assert decode(d=dims(scale=-1.0)) == SHAPE
     assert decode(out_dtype=7) == UNSUPPORTED
@@ -155,6 +155,7 @@ def test_prefill_validation():
     assert call(ws=P16 + 16) == ALIGN
     assert call(d=dims(Hk=3)) == SHAPE
     assert call(d=dims(dk=96, dv=96)) == UNSUPPORTED
+    assert call(d=dims(flags=8)) == UNSUPPORTED            # GDN_STREAM_STATE: decode only
     assert lib.gdn_prefill_chunked(ctypes.byref(d), 2, None, vp(P16), 230,
                                    ctypes.byref(inputs()), vp(P16), 0, vp(P16), vp(P16), need,
                                    None) == NULL

@@ -171,3 +171,38 @@ def test_fused_layer_multi_token_verify_b64(T):
     assert maxabs(f64(out).reshape(y.shape), y) <= TOL
     assert maxabs(f64(W["state_d"]), S) <= TOL
     assert maxabs(f64(cs_out), cs) == 0.0
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_stream_state_hint_is_bitwise_neutral(T):
+    """GDN_STREAM_STATE only changes the cache hints of the state loads and stores:
+    both decode entry points give the same bits with and without it, and match the
+    oracle."""
+    B = 4
+    W = to_dev(synth.decode_batch(seed=71 + T, B=B, Hk=2, Hv=4, T=T, head_map=synth.TILED))
+    Hk, Hv, dk, dv = W["Hk"], W["Hv"], W["dk"], W["dv"]
+    QK = Hk * dk
+    x = W["x_d"]
+    res = []
+    for hint in (False, True):
+        st, cs_out = W["state_d"].clone(), torch.empty_like(W["conv_state_d"])
+        out = ops.decode_layer(x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:], st, W["conv_w_d"],
+                               W["conv_state_d"], cs_out, Hk=Hk, Hv=Hv, dk=dk, dv=dv,
+                               head_map=W["head_map"], batch=B, tokens_per_seq=T, a=W["a_d"],
+                               b=W["b_d"], decay_param=W["A_log_d"], dt_bias=W["dt_bias_d"],
+                               z=W["z_d"], norm_weight=W["norm_w_d"], stream_state=hint)
+        y = ops.conv_update(x, W["conv_w_d"], W["conv_state_d"].clone(), num_seqs=B)
+        st2 = W["state_d"].clone()
+        out2 = ops.decode_step(y[:, :QK], y[:, QK:2 * QK], y[:, 2 * QK:], st2, Hk=Hk, Hv=Hv,
+                               dk=dk, dv=dv, head_map=W["head_map"], batch=B,
+                               tokens_per_seq=T, a=W["a_d"], b=W["b_d"],
+                               decay_param=W["A_log_d"], dt_bias=W["dt_bias_d"], z=W["z_d"],
+                               norm_weight=W["norm_w_d"], stream_state=hint)
+        res.append((out, st, cs_out, out2, st2))
+    torch.cuda.synchronize()
+    for plain, hinted in zip(*res):
+        assert torch.equal(plain, hinted)
+    y, cs, S = oracle_layer(W, B=B, T=T)
+    assert maxabs(f64(res[1][0]).reshape(y.shape), y) <= TOL
+    assert maxabs(f64(res[1][1]), S) <= TOL
+    assert maxabs(f64(res[1][2]), cs) == 0.0
