@@ -64,7 +64,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // not stay in the last-level cache between calls). At B=64 x 32 heads the plain
 // form is 10 % faster while the 128 MiB state stays in the Infinity Cache; on
 // streams past it (four rotating state sets, 48 layers at B=32) the hinted form is
-// 11 % faster. Hinting only the stores changes neither.
+// 11 % faster. Hinting only the stores, or only the loads, changes neither.
 template <bool NT>
 __device__ __forceinline__ float4 load_state4(const float *p)
 {
