@@ -20,9 +20,10 @@ throughput probe. Also reported on the same JSON line:
   * two_launch: the same step as gdn_conv_update then gdn_decode_step;
   * rotating: the step cycling through 4 independent state sets (537 MB,
     larger than the 256 MB Infinity Cache), so the state cannot stay cached;
+    timed with the GDN_STREAM_STATE cache hint and without it;
   * verify: multi-token verify decode (T = 2, 4, 8 tokens per call) at B=64;
   * deep_model: 48 layers per token at Hv=48, B=1 and B=32, uncaptured and as
-    one HIP graph;
+    one HIP graph; B=32 (4.8 GB of state) with GDN_STREAM_STATE;
   * prefill: chunked prefill tokens/s at B=1, T=4096; prefill_varlen: 8 packed
     sequences of 512..8192 tokens;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.

@@ -87,10 +87,6 @@ __device__ __forceinline__ float4 load_act4_t(const void *p, int64_t idx)
                        f16_bits_to_f32(w.y & 0xffffu), f16_bits_to_f32(w.y >> 16));
 }
 
-// One element of runtime dtype `dt`, read without a branch: the 32-bit word
-// holding it is loaded (the base pointer is 4-byte aligned -- the host checks),
-// then the conversion is selected. Split into the load and the conversion so a
-// caller can issue other loads in between.
 // A zero the compiler cannot see through, in a VGPR. Added to a workgroup-uniform
 // element index it keeps that load on the vector memory path: as a scalar load it
 // would need its own wait, which also holds back every vector load whose address
@@ -102,6 +98,10 @@ __device__ __forceinline__ int vgpr_zero()
     return z;
 }
 
+// One element of runtime dtype `dt`, read without a branch: the 32-bit word
+// holding it is loaded (the base pointer is 4-byte aligned -- the host checks),
+// then the conversion is selected. Split into the load and the conversion so a
+// caller can issue other loads in between.
 __device__ __forceinline__ uint32_t load_word_nb(const void *p, int64_t idx, int dt)
 {
     const int64_t byte = dt == DT_F32 ? idx * 4 : idx * 2;
