@@ -20,6 +20,8 @@
 // Kernels:
 //  1. plan_kernel   -- chunk table: 64-token chunks from each sequence's first
 //                      token (the last may be short; none straddles sequences).
+//                      Several sequences only: one sequence's chunk bounds are
+//                      closed-form and the kernels below compute them.
 //  2. prep_kernel   -- per (chunk, k-head), all chunks in parallel: q/k L2 norm,
 //                      the gram K K^T and Q K^T (f16 MFMA, Q K^T from hi + lo
 //                      parts), the normalised Q and K^T for the workspace; then for
@@ -228,8 +230,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
     const int Hv = hc.Hv, Hk = hc.Hk, G = Hv / Hk;
     const int chunk = blockIdx.x / Hk;
     const int kh = blockIdx.x % Hk;
-    const int tok0 = p.chunk_start[chunk];
-    const int n = p.chunk_len[chunk];
+    // one sequence covers tokens [0, total) (the host checks cu[0] = 0 and
+    // cu[N] = total): its chunk bounds need no table, and no plan kernel runs
+    const bool one_seq = p.N == 1;
+    const int tok0 = one_seq ? C * chunk : p.chunk_start[chunk];
+    const int n = one_seq ? min(C, p.total - C * chunk) : p.chunk_len[chunk];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const uint32_t flags = hc.flags;
@@ -760,19 +765,20 @@ __global__ __launch_bounds__(64 * (NW + 2), 1) void carry_kernel(PrefillParams p
     const int part = (id >> 3) % NG;
     if (group >= p.N * Hv)
         return;
-    const int seq = p.seq_order[group / Hv], h = group % Hv;
+    const bool one_seq = p.N == 1;  // tokens [0, total), no tables (see prep_kernel)
+    const int seq = one_seq ? 0 : p.seq_order[group / Hv], h = group % Hv;
     const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
     const int dvw = part * 16 * NW;  // the workgroup's first dv row
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
     const int dvl = dvw + wave * 16 + li;  // this lane's dv row
-    const int start = p.cu[seq];
-    const int len = p.cu[seq + 1] - start;
+    const int start = one_seq ? 0 : p.cu[seq];
+    const int len = one_seq ? p.total : p.cu[seq + 1] - start;
     const int nch = (len + C - 1) / C;
     if (nch == 0)
         return;  // empty sequence: state untouched
-    const int c0 = p.seq_chunk0[seq];
+    const int c0 = one_seq ? 0 : p.seq_chunk0[seq];
 
     if (wave >= NW) {
         // copy waves: every chunk's operands, one chunk ahead, into the ring
@@ -954,18 +960,19 @@ __global__ __launch_bounds__(64 * (2 * NW + 2), 1) void carry_split_kernel(Prefi
     const int part = (id >> 3) % NG;
     if (group >= p.N * Hv)
         return;
-    const int seq = p.seq_order[group / Hv], h = group % Hv;
+    const bool one_seq = p.N == 1;  // tokens [0, total), no tables (see prep_kernel)
+    const int seq = one_seq ? 0 : p.seq_order[group / Hv], h = group % Hv;
     const int kh = k_head_of(hc.head_map, h, hc.Hk, Hv);
     const int dvw = part * 16 * NW;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
-    const int start = p.cu[seq];
-    const int len = p.cu[seq + 1] - start;
+    const int start = one_seq ? 0 : p.cu[seq];
+    const int len = one_seq ? p.total : p.cu[seq + 1] - start;
     const int nch = (len + C - 1) / C;
     if (nch == 0)
         return;
-    const int c0 = p.seq_chunk0[seq];
+    const int c0 = one_seq ? 0 : p.seq_chunk0[seq];
 
     if (wave >= 2 * NW) {
         const int cw = wave - 2 * NW;
@@ -1228,7 +1235,8 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {
     if (p.num_chunks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
+    if (p.N > 1)  // one sequence: the chunk bounds are closed-form, no table
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
     const dim3 pgrid((unsigned)((int64_t)p.num_chunks * p.hc.Hk));
     switch (p.in.qkv_dt) {
     case DT_F32: hipLaunchKernelGGL((prep_kernel<DT_F32>), pgrid, dim3(256), 0, s, p); break;
