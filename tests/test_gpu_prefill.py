@@ -146,6 +146,18 @@ def test_varlen_prefill_then_64_decode_steps():
 
 # ------------------------------------------------------------------ edges, dtypes, gated norm
 
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_one_sequence_chunk_bounds(T):
+    """One sequence: its chunk bounds come from the token count alone (no chunk
+    table), including a lone partial chunk and an exact multiple of 64."""
+    P = synth.prefill(seed=20 + T, lengths=[T], Hk=2, Hv=4, head_map=synth.TILED, state_std=0.05)
+    out, st = run_prefill(P)
+    torch.cuda.synchronize()
+    y, S = oracle_seq(P, 0, f64(P["state"][0]))
+    assert maxabs(f64(out), y) <= TOL_OUT
+    assert maxabs(f64(st[0]), S) <= TOL_STATE
+
+
 @pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
 def test_ragged_lengths_including_empty(head_map):
     lengths = [0, 1, 63, 64, 65, 130, 0, 7]
@@ -228,8 +240,8 @@ def test_more_than_256_sequences():
 
 @pytest.mark.parametrize("act", [torch.float32, torch.float16])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_prefill_dtypes_and_gated_norm(act, out_dtype):
-    lengths = [100, 37]
+@pytest.mark.parametrize("lengths", [[100, 37], [137]])  # [137]: the one-sequence path
+def test_prefill_dtypes_and_gated_norm(act, out_dtype, lengths):
     P = synth.prefill(seed=12, lengths=lengths, Hk=2, Hv=4, head_map=synth.GROUPED, dtype=act,
                       state_std=0.02, with_z=True)
     out, st = run_prefill(P, out_dtype=out_dtype, gated=True)
