@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_fused(W, *, T, B, cs_in, cs_out, out_dtype=torch.float32, state=None, x=None, z=None,
-              a=None, b=None, slots=None, out=None):
+              a=None, b=None, slots=None, out=None, stream_state=False):
     Hk, Hv, dk, dv = W["Hk"], W["Hv"], W["dk"], W["dv"]
     QK = Hk * dk
     x = W["x_d"] if x is None else x
@@ -28,7 +28,7 @@ def run_fused(W, *, T, B, cs_in, cs_out, out_dtype=torch.float32, state=None, x=
                             b=W["b_d"] if b is None else b, decay_param=W["A_log_d"],
                             dt_bias=W["dt_bias_d"], z=W["z_d"] if z is None else z,
                             norm_weight=W["norm_w_d"], out_dtype=out_dtype, state_slots=slots,
-                            out=out)
+                            out=out, stream_state=stream_state)
 
 
 def test_fused_layer_conformance_fp16_split_and_oracle():
@@ -62,13 +62,16 @@ def test_fused_layer_conformance_fp16_split_and_oracle():
     assert maxabs(f64(st_full), f64(st2)) <= 1e-6
 
 
-def test_fused_layer_b64_steps_1_and_8():
+@pytest.mark.parametrize("stream_state", [False, True])
+def test_fused_layer_b64_steps_1_and_8(stream_state):
+    # the headline step, and (with the cache hint) the rotating leg's launch
     B = 64
     W = to_dev(synth.decode_batch(seed=2, B=B, head_map=synth.TILED))
     S_ref, cs_ref = f64(W["state"]), f64(W["conv_state"])
     bufs = [W["conv_state_d"].clone(), torch.empty_like(W["conv_state_d"])]
     for step in range(1, 9):
-        out = run_fused(W, T=1, B=B, cs_in=bufs[0], cs_out=bufs[1], out_dtype=torch.float32)
+        out = run_fused(W, T=1, B=B, cs_in=bufs[0], cs_out=bufs[1], out_dtype=torch.float32,
+                        stream_state=stream_state)
         bufs.reverse()
         y, cs_ref, S_ref = oracle_layer(W, B=B, T=1, state=S_ref, conv_state=cs_ref)
         if step in (1, 8):
@@ -145,13 +148,14 @@ def test_fused_layer_slots_and_out_of_range_slot():
 @pytest.mark.parametrize("B", [1, 32])
 def test_fused_layer_deep_model_shapes_hv48(B):
     # Hk=16, Hv=48: two of the independently seeded layers of the 48-layer stack,
-    # through the launch the 48-layer benchmark leg uses
+    # through the launch the 48-layer benchmark leg uses (with the cache hint at
+    # B=32, whose stack holds 4.8 GB of state)
     for layer in (0, 47):
         W = to_dev(synth.decode_batch(seed=4 * 1000 + layer, B=B, Hk=16, Hv=48,
                                       head_map=synth.TILED))
         cs_out = torch.empty_like(W["conv_state_d"])
         out = run_fused(W, T=1, B=B, cs_in=W["conv_state_d"], cs_out=cs_out,
-                        out_dtype=torch.float32)
+                        out_dtype=torch.float32, stream_state=B == 32)
         torch.cuda.synchronize()
         y, cs, S = oracle_layer(W, B=B, T=1)
         assert maxabs(f64(out).reshape(y.shape), y) <= TOL
