@@ -232,7 +232,7 @@ def verify_bench(torch, ops, synth, Ts=(2, 4, 8), calls=200, warmup=20):
 
 
 HEAD_SHAPES = ((32, 32), (64, 64), (96, 96), (128, 128), (64, 128), (128, 64), (128, 256),
-               (256, 128))
+               (256, 128), (256, 256))
 
 
 def head_shapes_bench(torch, ops, synth, calls=300, warmup=30):

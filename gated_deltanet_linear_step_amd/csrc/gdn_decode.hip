@@ -695,13 +695,14 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
 // count divides 64), each wave holds at most 64 rows, and the fused layer gives
 // every one of its 2 dk + dv conv channels a thread. A lane's share of the state
 // must fit its registers: 16 float4 pieces at 8 waves (256 VGPRs per lane), 8 at
-// 16 waves (128). dk = dv = 256 would need 16 pieces at 16 waves (768 conv
-// channels); built that way it spills about 300 bytes per lane, so it is not.
+// 16 waves (128). dk = dv = 256 takes 16 pieces at 16 waves (768 conv channels):
+// the one-token kernels fit (the fused layer spills 20 bytes per lane), the
+// multi-token ones spill 200-280 bytes per lane and run slower, still correct.
 bool decode_supported(int dk, int dv)
 {
     return (dk == 128 && dv == 128) || (dk == 64 && dv == 64) || (dk == 32 && dv == 32) ||
            (dk == 64 && dv == 128) || (dk == 128 && dv == 64) || (dk == 128 && dv == 256) ||
-           (dk == 256 && dv == 128) || (dk == 96 && dv == 96);
+           (dk == 256 && dv == 128) || (dk == 96 && dv == 96) || (dk == 256 && dv == 256);
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
@@ -738,6 +739,8 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
         return launch_decode_t<256, 128, 16>(p, s);
     if (dk == 96 && dv == 96)
         return launch_decode_t<96, 96, 6>(p, s);
+    if (dk == 256 && dv == 256)
+        return launch_decode_t<256, 256, 16>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -91,7 +91,7 @@ typedef struct gdn_dims {
     int32_t head_dim_k;  /* dk */
     int32_t head_dim_v;  /* dv. Built (dk, dv): decode step and layer (32,32), (64,64),
                             (96,96), (128,128), (64,128), (128,64), (128,256),
-                            (256,128);
+                            (256,128), (256,256);
                             chunked prefill (128,128). Others: UNSUPPORTED. */
     int32_t head_map;    /* gdn_head_map */
     int32_t decay;       /* gdn_decay, used with GDN_RAW_GATES */

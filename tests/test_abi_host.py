@@ -83,7 +83,7 @@ def test_decode_validation():
     assert decode(d=dims(Hk=3)) == SHAPE                    # Hv % Hk != 0
     assert decode(d=dims(Hk=0)) == SHAPE
     assert decode(d=dims(dk=96, dv=128)) == UNSUPPORTED     # not built
-    assert decode(d=dims(dk=256, dv=256)) == UNSUPPORTED
+    assert decode(d=dims(dk=256, dv=64)) == UNSUPPORTED
     assert decode(d=dims(dk=128, dv=32)) == UNSUPPORTED
     assert decode(d=dims(flags=16)) == UNSUPPORTED          # unknown flag bit
     assert decode(d=dims(head_map=2)) == SHAPE

@@ -141,7 +141,7 @@ def test_deep_model_layer_shapes_hv48(B):
 
 # every built (dk, dv) head shape
 HEAD_SHAPES = [(32, 32), (64, 64), (128, 128), (64, 128), (128, 64), (128, 256), (256, 128),
-               (96, 96)]
+               (96, 96), (256, 256)]
 
 
 @pytest.mark.parametrize("dk,dv", HEAD_SHAPES)

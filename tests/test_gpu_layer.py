@@ -83,7 +83,7 @@ def test_fused_layer_b64_steps_1_and_8(stream_state):
 
 @pytest.mark.parametrize("dk,dv,Hk,Hv", [(128, 128, 2, 4), (64, 64, 2, 2), (32, 32, 1, 4),
                                          (64, 128, 2, 2), (128, 64, 2, 4), (128, 256, 2, 4),
-                                         (256, 128, 1, 2), (96, 96, 2, 4)])
+                                         (256, 128, 1, 2), (96, 96, 2, 4), (256, 256, 1, 2)])
 @pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
 @pytest.mark.parametrize("T", [1, 3, 9, 17])
 def test_fused_layer_shapes_maps_tokens(dk, dv, Hk, Hv, head_map, T):
