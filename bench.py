@@ -20,13 +20,17 @@ throughput probe. Also reported on the same JSON line:
   * two_launch: the same step as gdn_conv_update then gdn_decode_step;
   * rotating: the step cycling through 4 independent state sets (537 MB,
     larger than the 256 MB Infinity Cache), so the state cannot stay cached;
-    timed with the GDN_STREAM_STATE cache hint and without it;
+    timed with the GDN_STREAM_STATE cache hint and without it, over 1000 steps
+    whatever --steps says; pct_hbm_peak_cache_free and roofline_cache_free come
+    from it (the headline's 128 MiB state partly stays in that cache);
   * verify: multi-token verify decode (T = 2, 4, 8 tokens per call) at B=64;
   * deep_model: 48 layers per token at Hv=48, B=1 and B=32, uncaptured and as
     one HIP graph; B=32 (4.8 GB of state) with GDN_STREAM_STATE;
   * prefill: chunked prefill tokens/s at B=1, T=4096; prefill_varlen: 8 packed
     sequences of 512..8192 tokens;
-  * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+  * cpu_baseline: the CPU oracle on the host cores (all the GPU's share, and one
+    thread): the decode step, the T=4096 and varlen prefill calls, the 48-layer
+    model per layer (extrapolated per token); the CPU model and nproc.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -44,6 +48,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 VARLEN_LENGTHS = (512, 1024, 2048, 3072, 4096, 5120, 6144, 8192)
+ROTATING_STEPS = 1000
 METRIC = "decode state GB/s (% HBM peak); prefill tokens/s at Hv=32,d=128"
 
 
@@ -154,11 +159,12 @@ def decode_bench(args, torch, ops, synth):
     value = state_bytes / (ms_step * 1e-3) / 1e9
 
     # rotating variant: 4 state sets, > Infinity Cache; with GDN_STREAM_STATE (the
-    # caller's hint for exactly this case), then without it
+    # caller's hint for exactly this case), then without it. Its length does not
+    # follow --steps: ROTATING_STEPS steps (about 50 ms) always.
     for _ in range(nsets * 4):
         for S in sets:
             step(S, "layer_stream")
-    Kr = max(nsets, (K // nsets) * nsets)
+    Kr = ROTATING_STEPS
     ms_rot, _ = timed(lambda i: step(sets[i % nsets], "layer_stream"), Kr)
     for _ in range(nsets * 4):
         for S in sets:
@@ -168,17 +174,32 @@ def decode_bench(args, torch, ops, synth):
     src_hash = kernel_source_hash(["gdn_decode.hip", "gdn_device.h", "gdn_kernels.h"])
     traffic = read_traffic("decode_layer_b64_bf16_traffic.md", src_hash)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    rot_achieved = dec_bytes / (ms_rot * 1e-3) / 1e9
     res = dict(
         value=value, ms_per_step=ms_step, wall_s=wall,
+        state_residency="cache-resident: the 128 MiB state of this workload stays partly in "
+                        "the 256 MB Infinity Cache between steps; the rotating leg and "
+                        "roofline_cache_free give the rate with the state streamed from HBM",
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
+                      traffic_note="L2-to-fabric bytes (FETCH_SIZE + WRITE_SIZE, calibrated on a "
+                                   "copy); the counters do not tell Infinity-Cache hits from "
+                                   "HBM reads",
                       kernel="gdn decode_kernel<dk=128,dv=128,waves=8,bf16,conv K=4> "
                              "(gdn_decode_layer)", bytes_per_launch=dec_bytes,
-                      avg_launch_us=dec_ms * 1e3, kernel_source_sha256_16=src_hash),
+                      avg_launch_us=dec_ms * 1e3, kernel_source_sha256_16=src_hash,
+                      state="cache-resident (128 MiB, fits the 256 MB Infinity Cache)"),
+        roofline_cache_free=dict(bound="hbm", achieved=rot_achieved, peak=HBM_PEAK_GBS,
+                                 unit="GB/s", frac=rot_achieved / HBM_PEAK_GBS,
+                                 kernel="gdn decode_kernel<dk=128,dv=128,waves=16,bf16,conv K=4,"
+                                        "non-temporal> (gdn_decode_layer, GDN_STREAM_STATE)",
+                                 bytes_per_launch=dec_bytes, avg_launch_us=ms_rot * 1e3,
+                                 steps=Kr, state="streamed: 4 state sets, 537 MB, cycled"),
         two_launch=dict(step="gdn_conv_update + gdn_decode_step", ms_per_step=ms_two,
                         value=state_bytes / (ms_two * 1e-3) / 1e9, unit="GB/s"),
-        rotating=dict(sets=nsets, footprint_mb=nsets * (state_bytes // 2) / 1e6,
+        rotating=dict(sets=nsets, footprint_mb=nsets * (state_bytes // 2) / 1e6, steps=Kr,
                       stream_state=True, ms_per_step=ms_rot,
+                      pct_hbm_peak=100 * state_bytes / (ms_rot * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       value=state_bytes / (ms_rot * 1e-3) / 1e9, unit="GB/s",
                       ms_per_step_no_hint=ms_rot_plain,
                       value_no_hint=state_bytes / (ms_rot_plain * 1e-3) / 1e9),
@@ -431,34 +452,109 @@ def counter_pass(torch, ops, synth, steps=10, copy_mib=256):
           file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds):
-    """The f64 CPU oracle on the decode workload, B=64, for >= `seconds` of work."""
+    """The f64 CPU oracle as it stands, on the host cores, as a baseline only (never
+    the target): the B=64 decode step (the headline's unit, state GB/s) on all the
+    threads the host grants this GPU and on one thread; the T=4096 and the varlen
+    prefill calls whole; the 48-layer model per layer, extrapolated per token. The
+    oracle's drivers spread independent sequences (decode) or (sequence, v-head)
+    pairs (prefill) over threads; each unit is the sequential f64 recurrence."""
     import numpy as np
     import oracle
     from gated_deltanet_linear_step_amd import synth
 
+    f = lambda t: t.double().numpy()  # noqa: E731
+    nproc = os.cpu_count() or 1
+    threads = max(1, min(16, nproc))  # a one-GPU box's share of the host is 16 cores
+    res = dict(kind="oracle", cores=threads, nproc=nproc, cpu_model=cpu_model())
+
+    # --- the headline decode step: B=64, one token, conv + core, state GB/s
     B, Hk, Hv, d = 64, 16, 32, 128
     W = synth.decode_batch(seed=2, B=B, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED)
-    f = lambda t: t.double().numpy()  # noqa: E731
-    threads = max(1, min(16, os.cpu_count() or 1))
-    S, cs = f(W["state"]), f(W["conv_state"])
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        _, cs, S = oracle.batch(B=B, T=1, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=oracle.MAP_TILED,
-                                S0=S, a=f(W["a"]), b=f(W["b"]), decay_param=f(W["A_log"]),
-                                dt_bias=f(W["dt_bias"]), z=f(W["z"]), norm_w=f(W["norm_w"]),
-                                x=f(W["x"]), conv_w=f(W["conv_w"]), conv_state=cs,
-                                nthreads=threads)
-        steps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = (time.perf_counter() - t0) / steps
     state_bytes = 2 * B * Hv * d * d * 4
-    return dict(value=state_bytes / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                ms_per_step=dt * 1e3,
-                sample=f"{steps} decode steps of the B=64 workload (conv + core, f64 oracle, "
-                       f"{threads} threads over sequences); GB/s counts fp32 state bytes")
+
+    def decode_rate(nthreads, budget):
+        S, cs = f(W["state"]), f(W["conv_state"])
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            _, cs, S = oracle.batch(B=B, T=1, Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=oracle.MAP_TILED,
+                                    S0=S, a=f(W["a"]), b=f(W["b"]), decay_param=f(W["A_log"]),
+                                    dt_bias=f(W["dt_bias"]), z=f(W["z"]), norm_w=f(W["norm_w"]),
+                                    x=f(W["x"]), conv_w=f(W["conv_w"]), conv_state=cs,
+                                    nthreads=nthreads)
+            steps += 1
+            if time.perf_counter() - t0 >= budget:
+                return steps, (time.perf_counter() - t0) / steps
+
+    steps, dt = decode_rate(threads, 0.35 * seconds)
+    res.update(value=state_bytes / dt / 1e9, unit="GB/s", ms_per_step=dt * 1e3,
+               sample=f"{steps} decode steps of the B=64 workload (conv + core, f64 oracle, "
+                      f"{threads} threads over sequences); GB/s counts fp32 state bytes")
+    steps1, dt1 = decode_rate(1, 0.2 * seconds)
+    res["single_thread"] = dict(value=state_bytes / dt1 / 1e9, unit="GB/s", cores=1,
+                                ms_per_step=dt1 * 1e3, sample=f"{steps1} decode steps, one thread")
+
+    # --- the chunked-prefill workloads through the token-by-token oracle
+    def prefill_rate(P, nthreads, heads=None, seqs=None):
+        cu = [int(c) for c in P["cu_seqlens"]]
+        if seqs is not None:  # a prefix of the packed sequences
+            cu = cu[:seqs + 1]
+        T = cu[-1]
+        g = lambda t: f(t[:T])  # noqa: E731
+        t0 = time.perf_counter()
+        oracle.packed(g(P["q"]), g(P["k"]), g(P["v"]), f(P["state"][:len(cu) - 1]), P["head_map"],
+                      cu, a=g(P["a"]), b=g(P["b"]), decay_param=f(P["A_log"]),
+                      dt_bias=f(P["dt_bias"]), nthreads=nthreads, heads=heads)
+        dt = time.perf_counter() - t0
+        nh = Hv if heads is None else len(heads)
+        return T, dt, T * nh / Hv / dt  # tokens/s of a whole (all-heads) call
+
+    P3 = synth.prefill(seed=3, lengths=[4096], head_map=synth.GROUPED)
+    T3, dt3, rate3 = prefill_rate(P3, threads)
+    _, dt31, rate31 = prefill_rate(P3, 1, heads=[0, 1])
+    res["prefill_t4096"] = dict(value=rate3, unit="tokens/s", cores=threads, s_per_call=dt3,
+                                sample="one whole T=4096 call, all 32 v-heads",
+                                single_thread=dict(value=rate31, unit="tokens/s", cores=1,
+                                                   sample="2 of 32 v-heads of the T=4096 call on "
+                                                          "one thread, scaled to 32 (extrapolated)"))
+    P5 = synth.prefill(seed=5, lengths=list(VARLEN_LENGTHS), head_map=synth.TILED, state_std=0.02)
+    T5, dt5, rate5 = prefill_rate(P5, threads)
+    res["prefill_varlen"] = dict(value=rate5, unit="tokens/s", cores=threads, s_per_call=dt5,
+                                 sample=f"one whole varlen call: 8 sequences, {T5} tokens, "
+                                        "all 32 v-heads")
+
+    # --- the 48-layer model, per layer, extrapolated per token
+    deep = {}
+    for Bd in (1, 32):
+        Ld = synth.decode_batch(seed=4000, B=Bd, Hk=16, Hv=48, dk=d, dv=d, head_map=synth.TILED)
+        S, cs = f(Ld["state"]), f(Ld["conv_state"])
+        n, t0 = 0, time.perf_counter()
+        while n < 1 or time.perf_counter() - t0 < 0.05 * seconds:
+            _, cs, S = oracle.batch(B=Bd, T=1, Hk=16, Hv=48, dk=d, dv=d, head_map=oracle.MAP_TILED,
+                                    S0=S, a=f(Ld["a"]), b=f(Ld["b"]), decay_param=f(Ld["A_log"]),
+                                    dt_bias=f(Ld["dt_bias"]), z=f(Ld["z"]), norm_w=f(Ld["norm_w"]),
+                                    x=f(Ld["x"]), conv_w=f(Ld["conv_w"]), conv_state=cs,
+                                    nthreads=threads)
+            n += 1
+        per_layer = (time.perf_counter() - t0) / n
+        sb = 2 * 48 * Bd * 48 * d * d * 4
+        deep[f"B{Bd}"] = dict(ms_per_layer=per_layer * 1e3, ms_per_token_step=48 * per_layer * 1e3,
+                              state_GBps=sb / (48 * per_layer) / 1e9, layers_timed=n,
+                              sample=f"{n} layer steps timed, extrapolated to 48 layers per "
+                                     "token (extrapolated)")
+    res["deep_model"] = dict(cores=threads, **deep)
+    return res
 
 
 def main():
@@ -466,7 +562,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU baseline's decode and deep-model legs; the "
+                         "prefill legs are whole calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true",
@@ -503,8 +601,10 @@ def main():
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
                 data="synthetic", config=dec["config"],
                 pct_hbm_peak=round(100 * dec["value"] / HBM_PEAK_GBS, 2),
-                roofline=dec["roofline"], two_launch=dec["two_launch"],
-                rotating=dec["rotating"])
+                pct_hbm_peak_cache_free=round(dec["rotating"]["pct_hbm_peak"], 2),
+                state_residency=dec["state_residency"],
+                roofline=dec["roofline"], roofline_cache_free=dec["roofline_cache_free"],
+                two_launch=dec["two_launch"], rotating=dec["rotating"])
     if not args.no_verify:
         print("[bench] multi-token verify decode, T=2,4,8", file=sys.stderr, flush=True)
         line["verify"] = verify_bench(torch, ops, synth)

@@ -70,8 +70,9 @@ gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dty
             return GDN_ERR_UNSUPPORTED;
         if (d->decay != GDN_DECAY_LOG_RATE && d->decay != GDN_DECAY_NEGATIVE_RATE)
             return GDN_ERR_SHAPE;
-        if (!aligned(in->a, 4) || !aligned(in->b, 4))
-            return GDN_ERR_ALIGN;  // gates are read as aligned 32-bit words
+        const int64_t gs = dtype_size(in->ab_dtype);
+        if (!aligned(in->a, gs) || !aligned(in->b, gs))
+            return GDN_ERR_ALIGN;  // gate elements are read whole, never past the last one
     } else if (!in->g || !in->beta) {
         return GDN_ERR_NULL;
     } else if (!aligned(in->g, 4) || !aligned(in->beta, 4)) {
@@ -159,7 +160,54 @@ const char *gdn_status_string(gdn_status s)
     return "unknown status";
 }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 200; }
+
+gdn_status gdn_decode_launch_info(const gdn_dims *d, int32_t batch, int32_t tokens_per_seq,
+                                  int32_t fused_conv, gdn_launch_info *info)
+{
+    if (!d || !info)
+        return GDN_ERR_NULL;
+    if (d->num_k_heads < 1 || d->num_v_heads < 1 || d->num_v_heads % d->num_k_heads != 0 ||
+        batch < 0 || tokens_per_seq < 1)
+        return GDN_ERR_SHAPE;
+    if ((d->flags & ~kDecodeFlags) != 0 || !gdn::decode_supported(d->head_dim_k, d->head_dim_v))
+        return GDN_ERR_UNSUPPORTED;
+    const gdn::DecodePlan pl = gdn::decode_plan(d->head_dim_k, d->head_dim_v, batch, tokens_per_seq,
+                                                d->num_v_heads, fused_conv != 0, d->flags);
+    *info = gdn_launch_info{};
+    info->waves = pl.waves;
+    info->lanes_per_row = pl.lanes_per_row;
+    info->token_mode = pl.mode;
+    info->nontemporal = pl.nontemporal;
+    info->workgroups = pl.workgroups;
+    info->threads = pl.threads;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_launch_info(const gdn_dims *d, int32_t num_seqs, const int32_t *cu_seqlens_host,
+                                   int32_t total_tokens, int32_t compute_units, gdn_launch_info *info)
+{
+    if (!d || !info || !cu_seqlens_host)
+        return GDN_ERR_NULL;
+    if (d->num_k_heads < 1 || d->num_v_heads < 1 || d->num_v_heads % d->num_k_heads != 0 ||
+        num_seqs < 1 || total_tokens < 0 || compute_units < 1)
+        return GDN_ERR_SHAPE;
+    if ((d->flags & ~kPrefillFlags) != 0 || !gdn::prefill_supported(d->head_dim_k, d->head_dim_v))
+        return GDN_ERR_UNSUPPORTED;
+    int64_t chunks = 0, max_chunks = 0;
+    const gdn_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens, &chunks, &max_chunks);
+    if (st != GDN_OK)
+        return st;
+    const gdn::PrefillPlan pl = gdn::prefill_plan(num_seqs, d->num_k_heads, d->num_v_heads,
+                                                  d->head_dim_k, d->head_dim_v, chunks, compute_units);
+    *info = gdn_launch_info{};
+    info->carry_kind = pl.carry_kind;
+    info->slices_per_workgroup = pl.slices_per_wg;
+    info->workgroups = pl.carry_workgroups;
+    info->threads = pl.carry_threads;
+    info->prep_workgroups = pl.prep_workgroups;
+    return GDN_OK;
+}
 
 gdn_status gdn_conv_update(int32_t channels, int32_t kernel_size, int32_t num_seqs,
                            const int32_t *cu_seqlens, int32_t total_tokens, int32_t x_dtype,

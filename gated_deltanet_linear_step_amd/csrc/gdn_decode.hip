@@ -92,7 +92,8 @@ __device__ __forceinline__ void store_state4(float *p, float4 s)
 template <int QT, int PPR>
 struct TokenRaw {
     Raw4<QT> k[PPR], q[PPR];
-    uint32_t ga, gb, v;
+    GateWord ga, gb;
+    uint32_t v;
 };
 
 // piece m of a lane that holds columns col + 4 LPR m of a row
@@ -112,8 +113,8 @@ __device__ __forceinline__ void load_token(TokenRaw<QT, PPR> &t, const DecodePar
     const bool raw = p.hc.flags & F_RAW_GATES;
     const int gdt = raw ? in.ab_dt : DT_F32;
     const int64_t gi = r * Hv + h + vgpr_zero();  // a vector load (see vgpr_zero)
-    t.ga = load_word_nb(raw ? in.a : (const void *)in.g, gi, gdt);
-    t.gb = load_word_nb(raw ? in.b : (const void *)in.beta, gi, gdt);
+    t.ga = load_gate(raw ? in.a : (const void *)in.g, gi, gdt);
+    t.gb = load_gate(raw ? in.b : (const void *)in.beta, gi, gdt);
     if constexpr (QKV)
         t.v = load_raw1<QT>(in.v, r * in.v_stride + (int64_t)h * DV + vrow);
 }
@@ -539,8 +540,7 @@ __global__ __launch_bounds__(NW * 64, (decode_min_waves<DK, DV, NW>())) void dec
             beta = sc_s[tt][4];
         } else {
             float ik, iq;
-            token_scalars(kk, qq, word_to_f32(tr.ga, r * Hv + h, gdt), word_to_f32(tr.gb, r * Hv + h, gdt),
-                          ik, iq, kq, alpha, beta);
+            token_scalars(kk, qq, gate_value(tr.ga, gdt), gate_value(tr.gb, gdt), ik, iq, kq, alpha, beta);
         }
 #pragma unroll
         for (int rr = 0; rr < RPL; ++rr) {
@@ -658,34 +658,35 @@ void launch_decode_nt(const DecodeParams &p, hipStream_t s)
     }
 }
 
-template <int DK, int DV, int NW, int CK, int MODE>
-void launch_decode_mode(const DecodeParams &p, hipStream_t s)
-{
-    if (p.hc.flags & F_STREAM_STATE)
-        launch_decode_nt<DK, DV, NW, CK, MODE, true>(p, s);
-    else
-        launch_decode_nt<DK, DV, NW, CK, MODE, false>(p, s);
-}
-
 template <int DK, int DV, int NW, int CK>
-void launch_decode_ck(const DecodeParams &p, hipStream_t s)
+void launch_decode_ck(const DecodeParams &p, const DecodePlan &pl, hipStream_t s)
 {
-    if (p.T == 1)
-        launch_decode_mode<DK, DV, NW, CK, MODE_ONE>(p, s);
-    else if constexpr (CK > 0)
-        launch_decode_mode<DK, DV, NW, CK, MODE_GROUP>(p, s);
-    else
-        launch_decode_mode<DK, DV, NW, CK, MODE_ANY>(p, s);
+    // the mode and the hint come from the plan; both are compile-time in the kernel
+    if (pl.mode == MODE_ONE) {
+        if (pl.nontemporal)
+            launch_decode_nt<DK, DV, NW, CK, MODE_ONE, true>(p, s);
+        else
+            launch_decode_nt<DK, DV, NW, CK, MODE_ONE, false>(p, s);
+    } else if constexpr (CK > 0) {
+        if (pl.nontemporal)
+            launch_decode_nt<DK, DV, NW, CK, MODE_GROUP, true>(p, s);
+        else
+            launch_decode_nt<DK, DV, NW, CK, MODE_GROUP, false>(p, s);
+    } else {
+        if (pl.nontemporal)
+            launch_decode_nt<DK, DV, NW, CK, MODE_ANY, true>(p, s);
+        else
+            launch_decode_nt<DK, DV, NW, CK, MODE_ANY, false>(p, s);
+    }
 }
 
 template <int DK, int DV, int NW>
-hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
+void launch_decode_t(const DecodeParams &p, const DecodePlan &pl, hipStream_t s)
 {
     if (p.conv_k == 4)
-        launch_decode_ck<DK, DV, NW, 4>(p, s);
+        launch_decode_ck<DK, DV, NW, 4>(p, pl, s);
     else
-        launch_decode_ck<DK, DV, NW, 0>(p, s);
-    return hipGetLastError();
+        launch_decode_ck<DK, DV, NW, 0>(p, pl, s);
 }
 
 }  // namespace
@@ -698,11 +699,36 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s)
 // 16 waves (128). dk = dv = 256 takes 16 pieces at 16 waves (768 conv channels):
 // the one-token kernels fit (the fused layer spills 20 bytes per lane), the
 // multi-token ones spill 200-280 bytes per lane and run slower, still correct.
-bool decode_supported(int dk, int dv)
+bool decode_supported(int dk, int dv) { return decode_plan(dk, dv, 1, 1, 1, false, 0).waves > 0; }
+
+// Waves per workgroup for each built shape. The 128 x 128 state takes 8 waves of 16
+// rows, except streamed one-token calls (GDN_STREAM_STATE): 16 waves of 8 rows, two
+// workgroups per CU at 63 VGPRs. On states past the Infinity Cache that is 4 %
+// faster than 8 waves (rotating sets 49.9 -> 47.7 us, 48 layers at B=32 1.83 ->
+// 1.79 ms); on cached states and at B=1 it is slower, so unhinted calls keep 8
+// waves. Same arithmetic, same bits.
+DecodePlan decode_plan(int dk, int dv, int B, int T, int Hv, bool fused_conv, uint32_t flags)
 {
-    return (dk == 128 && dv == 128) || (dk == 64 && dv == 64) || (dk == 32 && dv == 32) ||
-           (dk == 64 && dv == 128) || (dk == 128 && dv == 64) || (dk == 128 && dv == 256) ||
-           (dk == 256 && dv == 128) || (dk == 96 && dv == 96) || (dk == 256 && dv == 256);
+    DecodePlan pl{};
+    const bool nt = (flags & F_STREAM_STATE) != 0;
+    if (dk == 128 && dv == 128)
+        pl.waves = nt && T == 1 ? 16 : GDN_DECODE_NW;
+    else if ((dk == 64 && dv == 64) || (dk == 32 && dv == 32))
+        pl.waves = 4;
+    else if (dk == 96 && dv == 96)
+        pl.waves = 6;
+    else if ((dk == 64 && dv == 128) || (dk == 128 && dv == 64) || (dk == 128 && dv == 256))
+        pl.waves = 8;
+    else if ((dk == 256 && dv == 128) || (dk == 256 && dv == 256))
+        pl.waves = 16;
+    else
+        return DecodePlan{};  // not built: waves == 0
+    pl.lanes_per_row = dk == 128 ? GDN_DECODE_LPR128 : dk == 256 ? GDN_DECODE_LPR256 : dk == 96 ? 8 : dk / 4;
+    pl.mode = T == 1 ? MODE_ONE : fused_conv ? MODE_GROUP : MODE_ANY;
+    pl.nontemporal = nt ? 1 : 0;
+    pl.workgroups = B * Hv;
+    pl.threads = 64 * pl.waves;
+    return pl;
 }
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
@@ -710,38 +736,37 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t s)
     if (p.B == 0 || p.num_slots == 0)  // no slots: every sequence is a sentinel
         return hipSuccess;
     const int dk = p.hc.dk, dv = p.hc.dv;
+    const DecodePlan pl = decode_plan(dk, dv, p.B, p.T, p.hc.Hv, p.conv_k == 4, p.hc.flags);
     if (dk == 128 && dv == 128) {
-        // Streamed one-token calls (GDN_STREAM_STATE): 16 waves of 8 rows, two
-        // workgroups per CU at 63 VGPRs. On states past the Infinity Cache this is
-        // 4 % faster than 8 waves (rotating sets 49.9 -> 47.7 us, 48 layers at B=32
-        // 1.83 -> 1.79 ms); on cached states and at B=1 it is slower, so the
-        // unhinted calls keep 8 waves. Same arithmetic, same bits.
-        if ((p.hc.flags & F_STREAM_STATE) && p.T == 1) {
+        if (pl.waves == 16) {
+            // only instantiated for streamed one-token calls
             if (p.conv_k == 4)
                 launch_decode_nt<128, 128, 16, 4, MODE_ONE, true>(p, s);
             else
                 launch_decode_nt<128, 128, 16, 0, MODE_ONE, true>(p, s);
-            return hipGetLastError();
+        } else {
+            launch_decode_t<128, 128, GDN_DECODE_NW>(p, pl, s);
         }
-        return launch_decode_t<128, 128, GDN_DECODE_NW>(p, s);
+    } else if (dk == 64 && dv == 64) {
+        launch_decode_t<64, 64, 4>(p, pl, s);
+    } else if (dk == 32 && dv == 32) {
+        launch_decode_t<32, 32, 4>(p, pl, s);
+    } else if (dk == 64 && dv == 128) {
+        launch_decode_t<64, 128, 8>(p, pl, s);
+    } else if (dk == 128 && dv == 64) {
+        launch_decode_t<128, 64, 8>(p, pl, s);
+    } else if (dk == 128 && dv == 256) {
+        launch_decode_t<128, 256, 8>(p, pl, s);
+    } else if (dk == 256 && dv == 128) {
+        launch_decode_t<256, 128, 16>(p, pl, s);
+    } else if (dk == 96 && dv == 96) {
+        launch_decode_t<96, 96, 6>(p, pl, s);
+    } else if (dk == 256 && dv == 256) {
+        launch_decode_t<256, 256, 16>(p, pl, s);
+    } else {
+        return hipErrorInvalidValue;
     }
-    if (dk == 64 && dv == 64)
-        return launch_decode_t<64, 64, 4>(p, s);
-    if (dk == 32 && dv == 32)
-        return launch_decode_t<32, 32, 4>(p, s);
-    if (dk == 64 && dv == 128)
-        return launch_decode_t<64, 128, 8>(p, s);
-    if (dk == 128 && dv == 64)
-        return launch_decode_t<128, 64, 8>(p, s);
-    if (dk == 128 && dv == 256)
-        return launch_decode_t<128, 256, 8>(p, s);
-    if (dk == 256 && dv == 128)
-        return launch_decode_t<256, 128, 16>(p, s);
-    if (dk == 96 && dv == 96)
-        return launch_decode_t<96, 96, 6>(p, s);
-    if (dk == 256 && dv == 256)
-        return launch_decode_t<256, 256, 16>(p, s);
-    return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -84,10 +84,25 @@ struct PrefillParams {
     float *onorm;          // [total][Hv][dv]            f32 core output (gated norm only)
 };
 
+// Which decode kernel a call runs: waves per workgroup, lanes per state row, token
+// mode (0 any count, 1 fused-layer token groups, 2 one token), non-temporal state
+// access, workgroups and threads per workgroup. launch_decode launches exactly this.
+struct DecodePlan {
+    int waves, lanes_per_row, mode, nontemporal, workgroups, threads;
+};
 bool decode_supported(int dk, int dv);
+DecodePlan decode_plan(int dk, int dv, int B, int T, int Hv, bool fused_conv, uint32_t flags);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
+// Which carry kernel a prefill runs: kind 0 = carry_split (compute and output waves
+// per slice), 1 = carry (one wave per slice); dv slices of 16 rows per workgroup;
+// carry workgroups and threads per workgroup; prep workgroups. launch_prefill
+// launches exactly this for the device's compute-unit count.
+struct PrefillPlan {
+    int carry_kind, slices_per_wg, carry_workgroups, carry_threads, prep_workgroups;
+};
 bool prefill_supported(int dk, int dv);
+PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chunks, int cus);
 size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                int64_t total_tokens, bool norm);
 void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks);

@@ -845,7 +845,10 @@ __global__ __launch_bounds__(64 * (NW + 2), 1) void carry_kernel(PrefillParams p
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             er[j] = *reinterpret_cast<const f32x4 *>(&cur.gd[C + 16 * j + 4 * lg]);
-        const f32x4 g3 = *reinterpret_cast<const f32x4 *>(&cur.gd[48 + 4 * lg]);
+        // gamma_last = gamma_{C-1} (tokens past a short chunk carry G_{n-1}): one
+        // broadcast LDS read. Taking it from lane 48's copy of a 16-byte row read
+        // (readlane of element 3) was compiled into a read of element 0, gamma_{C-4}.
+        const float gl = cur.gd[C - 1];
         half8 sb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -881,8 +884,6 @@ __global__ __launch_bounds__(64 * (NW + 2), 1) void carry_kernel(PrefillParams p
             dl[ks] = pack_tiles(ar, br);
             dnl[ks] = pack_tiles(pr, qr);
         }
-        // gamma_last = gamma_{C-1}: lane 48 holds it as the last entry of its row
-        const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g3[3]), 48));
         __builtin_amdgcn_sched_barrier(0);
 
         // phase 4: S^T <- gamma_last S^T + K^T (D e), with the output's operands read behind
@@ -1034,7 +1035,7 @@ __global__ __launch_bounds__(64 * (2 * NW + 2), 1) void carry_split_kernel(Prefi
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 er[j] = *reinterpret_cast<const f32x4 *>(&cur.gd[C + 16 * j + 4 * lg]);
-            const f32x4 g3 = *reinterpret_cast<const f32x4 *>(&cur.gd[48 + 4 * lg]);
+            const float gl = cur.gd[C - 1];  // gamma_last, a broadcast read (see carry_kernel)
             __builtin_amdgcn_sched_barrier(0);
 
             half8 kb[8][2];
@@ -1064,7 +1065,6 @@ __global__ __launch_bounds__(64 * (2 * NW + 2), 1) void carry_split_kernel(Prefi
                 xw[64 * (4 + ks)] = dn;
                 xw[64 * (6 + ks)] = pack_tiles(pr, qr);
             }
-            const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g3[3]), 48));
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): -D is published
             __builtin_amdgcn_s_barrier();        // B
 
@@ -1204,9 +1204,9 @@ void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
 }
 
 template <int NW>
-void launch_carry_split(const PrefillParams &p, int64_t groups, hipStream_t s)
+void launch_carry_split(const PrefillParams &p, const PrefillPlan &pl, hipStream_t s)
 {
-    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
+    const dim3 cgrid((unsigned)pl.carry_workgroups);
     const dim3 cblock(64 * (2 * NW + 2));
     const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
     switch (omode) {
@@ -1218,9 +1218,9 @@ void launch_carry_split(const PrefillParams &p, int64_t groups, hipStream_t s)
 }
 
 template <int NW>
-void launch_carry(const PrefillParams &p, int64_t groups, hipStream_t s)
+void launch_carry(const PrefillParams &p, const PrefillPlan &pl, hipStream_t s)
 {
-    const dim3 cgrid((unsigned)((groups + 7) / 8 * 8 * (DH / (16 * NW))));
+    const dim3 cgrid((unsigned)pl.carry_workgroups);
     const dim3 cblock(64 * (NW + 2));
     const int omode = (p.hc.flags & F_GATED_NORM) ? kOutNorm : p.out_dt;
     switch (omode) {
@@ -1231,36 +1231,60 @@ void launch_carry(const PrefillParams &p, int64_t groups, hipStream_t s)
     }
 }
 
+// Carry shape (each workgroup takes a whole CU's LDS): while one round of
+// workgroups covers every dv slice the call is bound by the per-chunk chain, so
+// the split carry runs with 1 slice per workgroup (8 per head) or, when that would
+// take two rounds, 2; beyond that it is throughput bound and the 4-slice carry,
+// which reads each chunk's shared operands once for 4 slices, is fastest.
+PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chunks, int cus)
+{
+    PrefillPlan pl{};
+    if (!prefill_supported(dk, dv))
+        return pl;
+    const int64_t groups = (int64_t)N * Hv;
+    const int64_t rounded = (groups + 7) / 8 * 8;  // XCD-aware order: groups in blocks of 8
+    if (groups * (DH / 16) <= cus) {
+        pl.carry_kind = 0;
+        pl.slices_per_wg = 1;
+        pl.carry_threads = 64 * (2 * 1 + 2);
+    } else if (groups * (DH / 32) <= cus) {
+        pl.carry_kind = 0;
+        pl.slices_per_wg = 2;
+        pl.carry_threads = 64 * (2 * 2 + 2);
+    } else {
+        pl.carry_kind = 1;
+        pl.slices_per_wg = 4;
+        pl.carry_threads = 64 * (4 + 2);
+    }
+    pl.carry_workgroups = (int)(rounded * (DH / (16 * pl.slices_per_wg)));
+    pl.prep_workgroups = (int)(num_chunks * Hk);
+    return pl;
+}
+
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {
     if (p.num_chunks == 0)
         return hipSuccess;
     if (p.N > 1)  // one sequence: the chunk bounds are closed-form, no table
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
-    const dim3 pgrid((unsigned)((int64_t)p.num_chunks * p.hc.Hk));
-    switch (p.in.qkv_dt) {
-    case DT_F32: hipLaunchKernelGGL((prep_kernel<DT_F32>), pgrid, dim3(256), 0, s, p); break;
-    case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
-    }
-    // Carry shape (each workgroup takes a whole CU's LDS): while one round of
-    // workgroups covers every dv slice the call is bound by the per-chunk chain,
-    // so the split carry runs with 1 slice per workgroup (8 per head) or, when
-    // that would take two rounds, 2; beyond that it is throughput bound and the
-    // 4-slice carry, which reads each chunk's shared operands once for 4 slices,
-    // is fastest.
-    const int64_t groups = (int64_t)p.N * p.hc.Hv;
     int cus = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (groups * (DH / 16) <= cus)
-        launch_carry_split<1>(p, groups, s);
-    else if (groups * (DH / 32) <= cus)
-        launch_carry_split<2>(p, groups, s);
+    const PrefillPlan pl = prefill_plan(p.N, p.hc.Hk, p.hc.Hv, p.hc.dk, p.hc.dv, p.num_chunks, cus);
+    const dim3 pgrid((unsigned)pl.prep_workgroups);
+    switch (p.in.qkv_dt) {
+    case DT_F32: hipLaunchKernelGGL((prep_kernel<DT_F32>), pgrid, dim3(256), 0, s, p); break;
+    case DT_F16: hipLaunchKernelGGL((prep_kernel<DT_F16>), pgrid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((prep_kernel<DT_BF16>), pgrid, dim3(256), 0, s, p); break;
+    }
+    if (pl.carry_kind == 0 && pl.slices_per_wg == 1)
+        launch_carry_split<1>(p, pl, s);
+    else if (pl.carry_kind == 0)
+        launch_carry_split<2>(p, pl, s);
     else
-        launch_carry<4>(p, groups, s);
+        launch_carry<4>(p, pl, s);
     if (p.hc.flags & F_GATED_NORM) {
         const int64_t rows = (int64_t)p.total * p.hc.Hv;
         hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);

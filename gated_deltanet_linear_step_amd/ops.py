@@ -27,7 +27,8 @@ L2NORM_QK, RAW_GATES, GATED_NORM, STREAM_STATE = 1, 2, 4, 8
 CHUNK = 64
 
 EXPORTED = ["gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
-            "gdn_prefill_chunked", "gdn_status_string", "gdn_version", "gdn_decode_layer"]
+            "gdn_prefill_chunked", "gdn_status_string", "gdn_version", "gdn_decode_layer",
+            "gdn_decode_launch_info", "gdn_prefill_launch_info"]
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _VP = ctypes.c_void_p
@@ -54,6 +55,15 @@ class Inputs(ctypes.Structure):
 class ConvArgs(ctypes.Structure):
     _fields_ = [("kernel_size", ctypes.c_int32), ("weight", _VP), ("state_in", _VP),
                 ("state_out", _VP)]
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("waves", "lanes_per_row", "token_mode", "nontemporal", "carry_kind",
+                 "slices_per_workgroup", "workgroups", "threads", "prep_workgroups")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class GdnError(RuntimeError):
@@ -97,6 +107,13 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill_chunked.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _VP, _VP,
                                         ctypes.c_int32, ctypes.POINTER(Inputs), _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.gdn_decode_launch_info.restype = ctypes.c_int
+    lib.gdn_decode_launch_info.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.POINTER(LaunchInfo)]
+    lib.gdn_prefill_launch_info.restype = ctypes.c_int
+    lib.gdn_prefill_launch_info.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _VP,
+                                            ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.POINTER(LaunchInfo)]
     _LIB = lib
     return lib
 
@@ -147,6 +164,58 @@ def _row_view(t, width: int, name: str):
     return t, t.stride(0)
 
 
+def _cu_device(cu, device):
+    """cu_seqlens as the device int32 [N+1] tensor the kernels read (a copy when the
+    caller's tensor has another dtype or lives elsewhere)."""
+    if cu is None:
+        return None
+    if cu.dtype.is_floating_point or cu.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d integer tensor")
+    return cu.to(device=device, dtype=torch.int32).contiguous()
+
+
+def _cu_host(cu):
+    """cu_seqlens as a host int32 [N+1] tensor (the prefill validates it there)."""
+    if cu.dtype.is_floating_point or cu.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d integer tensor")
+    return cu.to(device="cpu", dtype=torch.int32).contiguous()
+
+
+def _check_state(state, Hv, dv, dk):
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be contiguous float32")
+    if state.dim() != 4 or tuple(state.shape[1:]) != (Hv, dv, dk):
+        raise ValueError(f"state must be [slots][{Hv}][{dv}][{dk}], got {tuple(state.shape)}")
+
+
+def _check_out(out, rows, Hv, dv):
+    if out.dtype not in _DT or not out.is_contiguous():
+        raise ValueError("out must be contiguous f32, f16 or bf16")
+    if out.numel() != rows * Hv * dv or out.shape[0] != rows:
+        raise ValueError(f"out must be [{rows}][{Hv}][{dv}], got {tuple(out.shape)}")
+
+
+def _check_conv(conv_weight, conv_state_in, conv_state_out, qdtype, slots, channels):
+    K = conv_weight.shape[1] if conv_weight.dim() == 2 else -1
+    if tuple(conv_weight.shape) != (channels, K):
+        raise ValueError(f"conv_weight must be [{channels}][K]")
+    for name, t in (("conv_weight", conv_weight), ("conv_state_in", conv_state_in),
+                    ("conv_state_out", conv_state_out)):
+        if t.dtype != qdtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous in q's dtype")
+    for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+        if tuple(t.shape) != (slots, channels, K - 1):
+            raise ValueError(f"{name} must be [{slots}][{channels}][{K - 1}]")
+
+
+def _check_slots(state_slots, batch):
+    if state_slots is None:
+        return
+    if state_slots.dtype != torch.int32 or not state_slots.is_contiguous() or \
+            state_slots.numel() != batch:
+        raise ValueError(f"state_slots must be a contiguous int32 [{batch}] tensor")
+
+
 def make_dims(Hk, Hv, dk, dv, head_map, flags, decay=DECAY_LOG_RATE, scale=0.0, l2_eps=0.0,
               norm_eps=0.0) -> Dims:
     return Dims(Hk, Hv, dk, dv, head_map, decay, flags, scale, l2_eps, norm_eps)
@@ -188,6 +257,33 @@ def make_inputs(q, k, v, *, Hk, Hv, dk, dv, a=None, b=None, decay_param=None, dt
     return inp, keep
 
 
+def decode_launch_info(*, Hk, Hv, dk, dv, batch, tokens_per_seq=1, fused_conv=True,
+                       head_map=MAP_TILED, flags=L2NORM_QK | RAW_GATES | GATED_NORM) -> dict:
+    """The decode kernel gdn_decode_layer (fused_conv) or gdn_decode_step would run."""
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags)
+    info = LaunchInfo()
+    _check(load().gdn_decode_launch_info(ctypes.byref(dims), batch, tokens_per_seq,
+                                         int(fused_conv), ctypes.byref(info)),
+           "gdn_decode_launch_info")
+    return info.as_dict()
+
+
+def prefill_launch_info(lengths, *, Hk, Hv, dk, dv, compute_units, head_map=MAP_GROUPED,
+                        flags=L2NORM_QK | RAW_GATES) -> dict:
+    """The prefill kernels gdn_prefill_chunked would run for these sequence lengths
+    on a device with `compute_units` CUs."""
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags)
+    info = LaunchInfo()
+    _check(load().gdn_prefill_launch_info(ctypes.byref(dims), len(lengths), arr, cu[-1],
+                                          compute_units, ctypes.byref(info)),
+           "gdn_prefill_launch_info")
+    return info.as_dict()
+
+
 def conv_update(x, weight, conv_state, *, cu_seqlens=None, num_seqs=None, y=None,
                 y_dtype=torch.float32, stream=None):
     """Causal depthwise conv + SiLU over x [tokens][C] (rows may be strided),
@@ -201,8 +297,16 @@ def conv_update(x, weight, conv_state, *, cu_seqlens=None, num_seqs=None, y=None
         raise TypeError("weight and conv_state must have x's dtype")
     if not (weight.is_contiguous() and conv_state.is_contiguous()):
         raise ValueError("weight and conv_state must be contiguous")
+    if tuple(weight.shape) != (C, K) or tuple(conv_state.shape[1:]) != (C, K - 1) or \
+            conv_state.shape[0] < N:
+        raise ValueError("weight must be [C][K] and conv_state [N][C][K-1]")
+    cu_seqlens = _cu_device(cu_seqlens, x.device)
+    if cu_seqlens is not None and cu_seqlens.numel() != N + 1:
+        raise ValueError("cu_seqlens must hold N + 1 offsets")
     if y is None:
         y = torch.empty((total, C), dtype=y_dtype, device=x.device)
+    if y.dim() != 2 or y.shape[0] != total or y.shape[1] < C or y.stride(1) != 1:
+        raise ValueError("y must be [tokens][>= C] with contiguous channels")
     st = load().gdn_conv_update(C, K, N, _ptr(cu_seqlens), total, _dt(x), _ptr(x), x.stride(0),
                                 _ptr(weight), _ptr(conv_state), _dt(y), _ptr(y), y.stride(0),
                                 _stream(stream))
@@ -224,11 +328,12 @@ def decode_step(q, k, v, state, *, Hk, Hv, dk, dv, head_map, batch, tokens_per_s
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
                             norm_weight=norm_weight)
-    if state.dtype != torch.float32 or not state.is_contiguous():
-        raise ValueError("state must be contiguous float32")
+    _check_state(state, Hv, dv, dk)
     rows = batch * tokens_per_seq
     if out is None:
         out = torch.empty((rows, Hv, dv), dtype=out_dtype, device=state.device)
+    _check_out(out, rows, Hv, dv)
+    _check_slots(state_slots, batch)
     num_slots = state.shape[0]
     st = load().gdn_decode_step(ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(inp),
                                 _ptr(state), _ptr(state_slots), num_slots, _dt(out), _ptr(out),
@@ -254,17 +359,16 @@ def decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_out, *, 
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
                             norm_weight=norm_weight)
-    if state.dtype != torch.float32 or not state.is_contiguous():
-        raise ValueError("state must be contiguous float32")
-    for name, t in (("conv_weight", conv_weight), ("conv_state_in", conv_state_in),
-                    ("conv_state_out", conv_state_out)):
-        if t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous in q's dtype")
+    _check_state(state, Hv, dv, dk)
+    _check_conv(conv_weight, conv_state_in, conv_state_out, q.dtype, state.shape[0],
+                2 * Hk * dk + Hv * dv)
     conv = ConvArgs(conv_weight.shape[1], _ptr(conv_weight), _ptr(conv_state_in),
                     _ptr(conv_state_out))
     rows = batch * tokens_per_seq
     if out is None:
         out = torch.empty((rows, Hv, dv), dtype=out_dtype, device=state.device)
+    _check_out(out, rows, Hv, dv)
+    _check_slots(state_slots, batch)
     st = load().gdn_decode_layer(ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(conv),
                                  ctypes.byref(inp), _ptr(state), _ptr(state_slots), state.shape[0],
                                  _dt(out), _ptr(out), _stream(stream))
@@ -273,8 +377,13 @@ def decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_out, *, 
     return out
 
 
-def prefill_workspace_bytes(*, Hk, Hv, dk, dv, head_map=MAP_GROUPED, num_seqs, total_tokens):
-    dims = make_dims(Hk, Hv, dk, dv, head_map, 0)
+def prefill_workspace_bytes(*, Hk, Hv, dk, dv, head_map=MAP_GROUPED, num_seqs, total_tokens,
+                            gated_norm=False, flags=None):
+    """Workspace gdn_prefill_chunked needs; the gated norm needs more, so pass
+    gated_norm=True (or the call's flags) for calls that apply it."""
+    if flags is None:
+        flags = GATED_NORM if gated_norm else 0
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags)
     return int(load().gdn_prefill_workspace_bytes(ctypes.byref(dims), num_seqs, total_tokens))
 
 
@@ -290,20 +399,26 @@ def prefill_chunked(q, k, v, state, cu_seqlens, *, Hk, Hv, dk, dv, head_map, a=N
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
                             norm_weight=norm_weight)
-    if cu_seqlens_host is None:
-        cu_seqlens_host = cu_seqlens.to("cpu", torch.int32).contiguous()
-    cu_dev = cu_seqlens if cu_seqlens.is_cuda else cu_seqlens.to(state.device)
+    cu_seqlens_host = _cu_host(cu_seqlens if cu_seqlens_host is None else cu_seqlens_host)
+    cu_dev = _cu_device(cu_seqlens, state.device)
+    if cu_dev.numel() != cu_seqlens_host.numel():
+        raise ValueError("cu_seqlens and cu_seqlens_host differ in length")
     N = cu_seqlens_host.numel() - 1
     total = int(cu_seqlens_host[-1])
+    _check_state(state, Hv, dv, dk)
+    if state.shape[0] != N:
+        raise ValueError(f"state must hold one slot per sequence ({N})")
     if out is None:
         out = torch.empty((total, Hv, dv), dtype=out_dtype, device=state.device)
+    _check_out(out, total, Hv, dv)
     need = load().gdn_prefill_workspace_bytes(ctypes.byref(dims), N, total)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=state.device)
     host_ptr = ctypes.c_void_p(cu_seqlens_host.data_ptr())
     st = load().gdn_prefill_chunked(ctypes.byref(dims), N, host_ptr, _ptr(cu_dev), total,
                                     ctypes.byref(inp), _ptr(state), _dt(out), _ptr(out),
-                                    _ptr(workspace), workspace.numel(), _stream(stream))
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
     _check(st, "gdn_prefill_chunked")
     del keep
     return out
@@ -327,6 +442,7 @@ def prepare_conv_update(x, weight, conv_state, y, *, cu_seqlens=None, num_seqs=N
                         stream=None) -> PreparedCall:
     total, C = x.shape
     N = conv_state.shape[0] if num_seqs is None else num_seqs
+    cu_seqlens = _cu_device(cu_seqlens, x.device)
     args = (C, weight.shape[1], N, _ptr(cu_seqlens), total, _dt(x), _ptr(x), x.stride(0),
             _ptr(weight), _ptr(conv_state), _dt(y), _ptr(y), y.stride(0), _stream(stream))
     return PreparedCall(load().gdn_conv_update, args, "gdn_conv_update",
@@ -344,6 +460,9 @@ def prepare_decode_step(q, k, v, state, out, *, Hk, Hv, dk, dv, head_map, batch,
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
                             norm_weight=norm_weight)
+    _check_state(state, Hv, dv, dk)
+    _check_out(out, batch * tokens_per_seq, Hv, dv)
+    _check_slots(state_slots, batch)
     args = (ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(inp), _ptr(state),
             _ptr(state_slots), state.shape[0], _dt(out), _ptr(out), _stream(stream))
     return PreparedCall(load().gdn_decode_step, args, "gdn_decode_step",
@@ -361,6 +480,11 @@ def prepare_decode_layer(q, k, v, state, conv_weight, conv_state_in, conv_state_
     inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
                             decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
                             norm_weight=norm_weight)
+    _check_state(state, Hv, dv, dk)
+    _check_conv(conv_weight, conv_state_in, conv_state_out, q.dtype, state.shape[0],
+                2 * Hk * dk + Hv * dv)
+    _check_out(out, batch * tokens_per_seq, Hv, dv)
+    _check_slots(state_slots, batch)
     conv = ConvArgs(conv_weight.shape[1], _ptr(conv_weight), _ptr(conv_state_in),
                     _ptr(conv_state_out))
     args = (ctypes.byref(dims), batch, tokens_per_seq, ctypes.byref(conv), ctypes.byref(inp),
@@ -383,8 +507,11 @@ def prepare_prefill_chunked(q, k, v, state, cu_seqlens_dev, cu_seqlens_host, out
                             norm_weight=norm_weight)
     if cu_seqlens_host.device.type != "cpu" or cu_seqlens_host.dtype != torch.int32:
         raise ValueError("cu_seqlens_host must be a CPU int32 tensor")
+    cu_seqlens_dev = _cu_device(cu_seqlens_dev, state.device)
     N = cu_seqlens_host.numel() - 1
     total = int(cu_seqlens_host[-1])
+    _check_state(state, Hv, dv, dk)
+    _check_out(out, total, Hv, dv)
     args = (ctypes.byref(dims), N, ctypes.c_void_p(cu_seqlens_host.data_ptr()),
             _ptr(cu_seqlens_dev), total, ctypes.byref(inp), _ptr(state), _dt(out), _ptr(out),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))

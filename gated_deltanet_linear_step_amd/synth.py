@@ -6,12 +6,15 @@ Every array comes back as a torch CPU tensor in its storage dtype (f16, bf16,
 f32, int32); callers widen to float64 for the oracle and copy to the GPU for
 the HIP library.
 
-Two recipes:
+Three recipes:
 
 * ``sin_values`` -- f16/f32(sin(i * f) * amp), the deterministic patterns of the
   ferrum-kernels 0.8.0 test page (``half_values`` / ``float_values``), used for
   the T=4 layer conformance workload with the frequencies and amplitudes that
   page prints.
+* ``Lcg`` -- the 32-bit linear congruential draws of the ferrox-core 0.24.0
+  gdn.rs tests (``the_device_delta_step_matches_this_one``): un-normalised
+  uniform q, k, v and states, used for that test's device-step shapes.
 * numpy ``default_rng(seed)`` normals/uniforms rounded to bf16 (round to nearest
   even, via torch) for the batched-decode, prefill and deep-model workloads;
   draw order is parameters, then states, then per-step inputs.
@@ -157,3 +160,66 @@ def core_sin(T: int, Hk: int, Hv: int, dk: int, dv: int) -> dict:
         beta=torch.from_numpy(beta.astype(np.float32)).reshape(T, Hv),
         state=sin_values(Hv * dv * dk, 0.011, 0.025, torch.float32).reshape(Hv, dv, dk),
     )
+
+
+class Lcg:
+    """The ferrox-core gdn.rs test generator: seed <- seed * 1664525 + 1013904223
+    (mod 2^32); each draw is ((seed >> 8) / 2^23 - 1) * scale in f32, uniform in
+    [-scale, scale). Draws continue one stream in call order."""
+
+    def __init__(self, seed: int):
+        self.seed = seed & 0xFFFFFFFF
+
+    def draw(self, n: int, scale: float) -> np.ndarray:
+        out = np.empty(n, dtype=np.float32)
+        s = self.seed
+        for i in range(n):
+            s = (s * 1664525 + 1013904223) & 0xFFFFFFFF
+            out[i] = np.float32(s >> 8)
+        self.seed = s
+        return (out / np.float32(8388608.0) - np.float32(1.0)) * np.float32(scale)
+
+
+def device_step(n_k: int, n_v: int, s: int, seed: int = 12345) -> dict:
+    """The inputs of the ferrox-core device-step test for one token of one
+    sequence, drawn in that test's order: state [n_v][s][s] (scale 0.5), q, k
+    [n_k][s] and v [n_v][s] (scale 1), g = -|u| and beta = 0.5 + 0.25 u with u
+    uniform in [-1, 1). q and k are not normalised. f32 throughout."""
+    r = Lcg(seed)
+    state = r.draw(n_v * s * s, 0.5).reshape(n_v, s, s)
+    q = r.draw(n_k * s, 1.0).reshape(1, n_k, s)
+    k = r.draw(n_k * s, 1.0).reshape(1, n_k, s)
+    v = r.draw(n_v * s, 1.0).reshape(1, n_v, s)
+    g = -np.abs(r.draw(n_v, 1.0)).reshape(1, n_v)
+    beta = (np.float32(0.5) + np.float32(0.25) * r.draw(n_v, 1.0)).reshape(1, n_v)
+    t = torch.from_numpy
+    return dict(state=t(np.ascontiguousarray(state)), q=t(q), k=t(k), v=t(v),
+                g=t(np.ascontiguousarray(g, dtype=np.float32)),
+                beta=t(np.ascontiguousarray(beta, dtype=np.float32)), rng=r)
+
+
+def lcg_prefill(T: int, Hk: int, Hv: int, dk: int, dv: int, seed: int = 777,
+                qk_scale: float = 0.15) -> dict:
+    """An un-normalised prefill workload from the same LCG stream: q, k uniform in
+    [-qk_scale, qk_scale) (so |k|^2 is about dk * qk_scale^2 / 3, below 1 at
+    dk = 128 and the default scale: a stable delta rule without the in-op L2
+    norm), v in [-1, 1), g = -0.05 |u|, beta = 0.5 + 0.25 u, initial state in
+    [-0.05, 0.05). f32, one sequence."""
+    r = Lcg(seed)
+    state = r.draw(Hv * dv * dk, 0.05).reshape(1, Hv, dv, dk)
+    q = r.draw(T * Hk * dk, qk_scale).reshape(T, Hk, dk)
+    k = r.draw(T * Hk * dk, qk_scale).reshape(T, Hk, dk)
+    v = r.draw(T * Hv * dv, 1.0).reshape(T, Hv, dv)
+    g = np.float32(-0.05) * np.abs(r.draw(T * Hv, 1.0)).reshape(T, Hv)
+    beta = (np.float32(0.5) + np.float32(0.25) * r.draw(T * Hv, 1.0)).reshape(T, Hv)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))  # noqa: E731
+    return dict(T=T, Hk=Hk, Hv=Hv, dk=dk, dv=dv, q=t(q), k=t(k), v=t(v), g=t(g), beta=t(beta),
+                state=t(state), cu_seqlens=cu_seqlens([T]))
+
+
+def negative_rates(seed: int, Hv: int) -> torch.Tensor:
+    """Per-head decay rates for the negative-rate parameterisation (the rate that
+    multiplies softplus, passed as is): uniform in [-1, -0.135], the range that
+    A_log ~ U[-2, 0] gives under the log-rate form."""
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.uniform(-1.0, -0.135, Hv).astype(np.float32))

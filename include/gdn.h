@@ -113,18 +113,18 @@ typedef struct gdn_inputs {
     const void *q, *k, *v;
     int64_t q_stride, k_stride, v_stride;
     int32_t qkv_dtype;      /* gdn_dtype of q, k, v */
-    /* GDN_RAW_GATES: a, b [tokens][Hv] contiguous in ab_dtype; decay_param and
-     * dt_bias [Hv] f32. The decode reads 16-bit a, b by element pairs (the 4
-     * bytes from each even element index), so when tokens*Hv is odd the
-     * allocation must extend 2 bytes past the last element (allocations rounded
-     * to 4 bytes, as torch's are, satisfy this). */
+    /* GDN_RAW_GATES: a, b [tokens][Hv] contiguous in ab_dtype, aligned to their
+     * element size; decay_param and dt_bias [Hv] f32. Every read stays within
+     * the tokens*Hv elements. */
     const void *a, *b;
     int32_t ab_dtype;
     const float *decay_param, *dt_bias;
-    /* no GDN_RAW_GATES: g (log decay, <= 0 in a real layer) and beta [tokens][Hv] f32 */
+    /* no GDN_RAW_GATES: g (log decay, <= 0 in a real layer) and beta [tokens][Hv] f32,
+     * 4-byte aligned */
     const float *g, *beta;
-    /* GDN_GATED_NORM: z [tokens][Hv][dv] contiguous in z_dtype, 4-byte aligned;
-     * norm_weight [dv] f32 */
+    /* GDN_GATED_NORM: z [tokens][Hv][dv] contiguous in z_dtype, 4-byte aligned
+     * (read as 32-bit words; dv is even in every built shape, so no word reaches
+     * past the last element); norm_weight [dv] f32 */
     const void *z;
     int32_t z_dtype;
     const float *norm_weight;
@@ -177,7 +177,8 @@ gdn_status gdn_conv_update(int32_t channels, int32_t kernel_size, int32_t num_se
  *   num_slots       number of state slots (>= B when state_slots is NULL)
  *   out_dtype, out  [B*T][Hv][dv]; may not alias any input or the state
  * Errors: NULL, SHAPE, UNSUPPORTED (dims, dtype), OVERFLOW, ALIGN (q/k/v groups of 4
- * elements; a, b, g, beta, z and norm_weight to 4 bytes; the state to 16 bytes), LAUNCH.
+ * elements; a, b to their element size; g, beta, z and norm_weight to 4 bytes; the
+ * state to 16 bytes), LAUNCH.
  * ------------------------------------------------------------------------- */
 gdn_status gdn_decode_step(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
                            const gdn_inputs *in, float *state, const int32_t *state_slots,
@@ -211,6 +212,14 @@ typedef struct gdn_conv_args {
  * Every v-head workgroup computes the conv of the q/k channels it reads; the
  * new q/k window is written by one workgroup per k-head, which is why the
  * state is not updated in place.
+ * Slot pools: a call writes new windows only for the slots it names (and a
+ * live slot's window only to state_out); for every other slot state_out keeps
+ * what it held. A caller that alternates the two buffers while some calls do
+ * not name every slot must therefore carry the windows of the slots a call left
+ * out: e.g. copy those slots' windows from state_in to state_out after the
+ * call, or keep per slot which buffer holds its latest window and gather the
+ * windows of the next call's slots into the buffer passed as state_in. The
+ * delta state is updated in place and needs no such care.
  * Errors: those of gdn_decode_step; NULL (conv pointers), UNSUPPORTED (K),
  * ALIGN (conv buffers), SHAPE (state_out overlapping state_in).
  * ------------------------------------------------------------------------- */
@@ -252,6 +261,41 @@ gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
                                int32_t total_tokens, const gdn_inputs *in, float *state,
                                int32_t out_dtype, void *out, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel selection, for inspection and host-side tests. Which kernel a call runs
+ * follows from its shape and from the device, as the ferrum-kernels tests page
+ * checks for its own kernels (`chunk_k_gram_specialization_requires_repeated_
+ * k128_heads`, `simd_delta_specialization_is_shape_and_device_capability_driven`).
+ * These two calls report the choice the corresponding entry point makes, from the
+ * same code; they make no HIP call and launch nothing.
+ * ------------------------------------------------------------------------- */
+typedef struct gdn_launch_info {
+    int32_t waves;             /* decode: waves per workgroup */
+    int32_t lanes_per_row;     /* decode: lanes holding one dk-wide state row */
+    int32_t token_mode;        /* decode: 0 any token count, 1 token groups (fused layer,
+                                  T > 1), 2 one token per sequence */
+    int32_t nontemporal;       /* decode: 1 when GDN_STREAM_STATE selects the hinted kernel */
+    int32_t carry_kind;        /* prefill: 0 split carry (compute + output wave per dv
+                                  slice), 1 carry (one wave per slice) */
+    int32_t slices_per_workgroup; /* prefill: 16-row dv slices per carry workgroup */
+    int32_t workgroups;        /* grid of the decode kernel, or of the prefill carry */
+    int32_t threads;           /* threads per workgroup of that kernel */
+    int32_t prep_workgroups;   /* prefill: grid of the per-chunk preparation kernel */
+} gdn_launch_info;
+
+/* The decode kernel gdn_decode_step (fused_conv = 0) or gdn_decode_layer
+ * (fused_conv = 1) runs for these dims (flags included), batch and tokens_per_seq.
+ * Errors: NULL, SHAPE, UNSUPPORTED, as the entry points report them. */
+gdn_status gdn_decode_launch_info(const gdn_dims *dims, int32_t batch, int32_t tokens_per_seq,
+                                  int32_t fused_conv, gdn_launch_info *info);
+
+/* The kernels gdn_prefill_chunked runs for these dims and sequences on a device
+ * with `compute_units` CUs (the entry point queries the current device's count).
+ * cu_seqlens_host: host int32 [N+1]. Errors: NULL, SHAPE, UNSUPPORTED. */
+gdn_status gdn_prefill_launch_info(const gdn_dims *dims, int32_t num_seqs,
+                                   const int32_t *cu_seqlens_host, int32_t total_tokens,
+                                   int32_t compute_units, gdn_launch_info *info);
 
 /* Static, NUL-terminated description of a status code. */
 const char *gdn_status_string(gdn_status status);

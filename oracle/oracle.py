@@ -10,12 +10,13 @@ Sources, as cited in ``gdn_oracle.c``:
 """
 import ctypes
 import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 __all__ = [
     "lib_path", "load", "sigmoid", "silu", "softplus", "k_head", "l2norm", "gates",
-    "conv", "recurrence", "gated_rmsnorm", "core", "segment", "batch",
+    "conv", "recurrence", "gated_rmsnorm", "core", "segment", "batch", "packed",
     "MAP_GROUPED", "MAP_TILED", "DECAY_LOG_RATE", "DECAY_NEGATIVE_RATE",
 ]
 
@@ -36,7 +37,8 @@ class _CoreCfg(ctypes.Structure):
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "liboracle_gdn.so")
+    # GDN_ORACLE_LIB selects another build of the same source (the sanitized one)
+    return os.environ.get("GDN_ORACLE_LIB") or os.path.join(_HERE, "liboracle_gdn.so")
 
 
 def load():
@@ -257,3 +259,55 @@ def batch(*, B, T, Hk, Hv, dk, dv, head_map, S0, a, b, decay_param, dt_bias, z, 
         _p(_f64(dt_bias, (Hv,))), _p(_f64(z, (B, T, Hv, dv))), _p(_f64(norm_w, (dv,))), _p(S),
         _p(y))
     return y, cs, S
+
+
+def packed(q, k, v, S0, head_map, cu_seqlens, *, nthreads=1, heads=None, a=None, b=None,
+           decay_param=None, dt_bias=None, g=None, beta=None, z=None, norm_w=None,
+           l2norm_qk=True, decay_kind=DECAY_LOG_RATE, scale=None, l2_eps=1e-6, norm_eps=1e-6):
+    """Packed variable-length sequences (cu_seqlens [N+1]) through ``core``, token by
+    token. Each (sequence, v-head) pair is an independent problem: it is handed to
+    ``core`` as a one-k-head, one-v-head call on its own slices (the k-head the map
+    gives, that head's gates and parameters), and the pairs are spread over
+    ``nthreads`` host threads. This driver adds no arithmetic.
+    q, k [T][Hk][dk]; v [T][Hv][dv]; S0 [N][Hv][dv][dk]. Returns (y [T][Hv][dv],
+    S [N][Hv][dv][dk]); v-heads outside ``heads`` keep y = 0 and S = S0."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    N = len(cu) - 1
+    S = _f64(S0, (N, Hv, dv, dk)).copy()
+    y = np.zeros((T, Hv, dv))
+    raw = a is not None
+    if raw:
+        a, b = _f64(a, (T, Hv)), _f64(b, (T, Hv))
+        dp, db = _f64(decay_param, (Hv,)), _f64(dt_bias, (Hv,))
+    else:
+        g, beta = _f64(g, (T, Hv)), _f64(beta, (T, Hv))
+    if z is not None:
+        z = _f64(z, (T, Hv, dv))
+    heads = range(Hv) if heads is None else heads
+    units = [(i, h) for i in range(N) if cu[i + 1] > cu[i] for h in heads]
+
+    def one(unit):
+        i, h = unit
+        lo, hi = cu[i], cu[i + 1]
+        kh = k_head(head_map, h, Hk, Hv)
+        kw = dict(l2norm_qk=l2norm_qk, decay_kind=decay_kind, l2_eps=l2_eps, norm_eps=norm_eps,
+                  scale=1.0 / np.sqrt(dk) if scale is None else scale)
+        if raw:
+            kw.update(a=a[lo:hi, h:h + 1], b=b[lo:hi, h:h + 1], decay_param=dp[h:h + 1],
+                      dt_bias=db[h:h + 1])
+        else:
+            kw.update(g=g[lo:hi, h:h + 1], beta=beta[lo:hi, h:h + 1])
+        if z is not None:
+            kw.update(z=z[lo:hi, h:h + 1], norm_w=norm_w)
+        yh, Sh = core(q[lo:hi, kh:kh + 1], k[lo:hi, kh:kh + 1], v[lo:hi, h:h + 1],
+                      S[i, h:h + 1], MAP_GROUPED, **kw)
+        return unit, yh, Sh
+
+    with ThreadPoolExecutor(max_workers=max(1, int(nthreads))) as ex:
+        for (i, h), yh, Sh in ex.map(one, units):
+            y[cu[i]:cu[i + 1], h] = yh[:, 0]
+            S[i, h] = Sh[0]
+    return y, S

@@ -134,8 +134,15 @@ def test_prefill_validation():
     cu_tot = (ctypes.c_int32 * 3)(0, 100, 200)
     d = dims(head_map=ops.MAP_GROUPED)
     need = lib.gdn_prefill_workspace_bytes(ctypes.byref(d), 2, 230)
-    if need == 0:
-        pytest.skip("this build has no prefill kernels yet")
+    assert need > 0
+    # the gated norm keeps an f32 core output in the workspace: the query must say so
+    dn = dims(head_map=ops.MAP_GROUPED, flags=ops.GATED_NORM)
+    need_norm = lib.gdn_prefill_workspace_bytes(ctypes.byref(dn), 2, 230)
+    assert need_norm >= need + 230 * 4 * 128 * 4
+    assert ops.prefill_workspace_bytes(Hk=2, Hv=4, dk=128, dv=128, num_seqs=2, total_tokens=230,
+                                       gated_norm=True) == need_norm
+    assert ops.prefill_workspace_bytes(Hk=2, Hv=4, dk=128, dv=128, num_seqs=2,
+                                       total_tokens=230) == need
     # upper bound over splits: more sequences or tokens never need less
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(d), 3, 230) >= need
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(d), 2, 300) >= need
@@ -156,6 +163,8 @@ def test_prefill_validation():
     assert call(d=dims(Hk=3)) == SHAPE
     assert call(d=dims(dk=96, dv=96)) == UNSUPPORTED
     assert call(d=dims(flags=8)) == UNSUPPORTED            # GDN_STREAM_STATE: decode only
+    # a gated-norm call with the plain workspace size is refused, not overrun
+    assert call(d=dn, inp=inputs(z=vp(P16), norm_weight=vp(P16))) == WORKSPACE
     assert lib.gdn_prefill_chunked(ctypes.byref(d), 2, None, vp(P16), 230,
                                    ctypes.byref(inputs()), vp(P16), 0, vp(P16), vp(P16), need,
                                    None) == NULL
@@ -187,3 +196,92 @@ def test_layer_validation():
     assert layer(d=dims(Hk=3)) == SHAPE                     # the decode step's own checks
     assert layer(T=0) == SHAPE
     assert layer(inp=inputs(v_stride=2050)) == ALIGN
+
+
+# ------------------------------------------------------------------ kernel selection
+# Which kernel runs is a function of the shape, the flags and the device, checked
+# here on the host the way the ferrum-kernels tests page checks its specialisation
+# predicates (`simd_delta_specialization_is_shape_and_device_capability_driven`,
+# `chunk_k_gram_specialization_requires_repeated_k128_heads`).
+
+DECODE_SHAPES = {  # (dk, dv): (waves, lanes per row)
+    (32, 32): (4, 8), (64, 64): (4, 16), (96, 96): (6, 8), (128, 128): (8, 16),
+    (64, 128): (8, 16), (128, 64): (8, 16), (128, 256): (8, 16), (256, 128): (16, 32),
+    (256, 256): (16, 32)}
+
+
+@pytest.mark.parametrize("dk,dv", sorted(DECODE_SHAPES))
+def test_decode_kernel_choice_per_head_shape(dk, dv):
+    waves, lpr = DECODE_SHAPES[(dk, dv)]
+    for fused in (False, True):
+        for T, mode in ((1, 2), (4, 1 if fused else 0)):
+            i = ops.decode_launch_info(Hk=4, Hv=8, dk=dk, dv=dv, batch=3, tokens_per_seq=T,
+                                       fused_conv=fused)
+            assert (i["waves"], i["lanes_per_row"], i["token_mode"]) == (waves, lpr, mode)
+            assert i["workgroups"] == 3 * 8 and i["threads"] == 64 * waves
+            assert i["nontemporal"] == 0
+    # the geometry the kernel template asserts: a row's pieces tile dk, rows tile a wave
+    rows_per_load = 64 // lpr
+    assert 64 % lpr == 0 and dk % (4 * lpr) == 0
+    assert (dv // waves) % rows_per_load == 0 and dv // waves <= 64
+    assert 2 * dk + dv <= 64 * waves  # the fused layer gives every conv channel a thread
+
+
+def test_decode_stream_hint_selects_the_nontemporal_kernel():
+    f = ops.L2NORM_QK | ops.RAW_GATES | ops.GATED_NORM
+    one = ops.decode_launch_info(Hk=16, Hv=32, dk=128, dv=128, batch=64, flags=f | ops.STREAM_STATE)
+    assert (one["waves"], one["nontemporal"], one["token_mode"]) == (16, 1, 2)
+    multi = ops.decode_launch_info(Hk=16, Hv=32, dk=128, dv=128, batch=64, tokens_per_seq=4,
+                                   flags=f | ops.STREAM_STATE)
+    assert (multi["waves"], multi["nontemporal"], multi["token_mode"]) == (8, 1, 1)
+    other = ops.decode_launch_info(Hk=16, Hv=32, dk=64, dv=64, batch=64, flags=f | ops.STREAM_STATE)
+    assert (other["waves"], other["nontemporal"]) == (4, 1)
+    plain = ops.decode_launch_info(Hk=16, Hv=32, dk=128, dv=128, batch=64, flags=f)
+    assert (plain["waves"], plain["nontemporal"]) == (8, 0)
+
+
+def test_decode_launch_info_rejects_what_the_entry_points_reject():
+    with pytest.raises(ops.GdnError) as e:
+        ops.decode_launch_info(Hk=4, Hv=8, dk=128, dv=32, batch=1)
+    assert e.value.status == UNSUPPORTED
+    with pytest.raises(ops.GdnError) as e:
+        ops.decode_launch_info(Hk=3, Hv=8, dk=128, dv=128, batch=1)
+    assert e.value.status == SHAPE
+    with pytest.raises(ops.GdnError) as e:
+        ops.decode_launch_info(Hk=4, Hv=8, dk=128, dv=128, batch=1, tokens_per_seq=0)
+    assert e.value.status == SHAPE
+
+
+def test_prefill_carry_choice_follows_sequences_and_compute_units():
+    kw = dict(Hk=16, Hv=32, dk=128, dv=128)
+    # one 4096-token sequence: 32 heads x 8 one-slice workgroups fill 256 CUs once
+    i = ops.prefill_launch_info([4096], compute_units=256, **kw)
+    assert (i["carry_kind"], i["slices_per_workgroup"]) == (0, 1)
+    assert i["workgroups"] == 256 and i["threads"] == 64 * 4 and i["prep_workgroups"] == 64 * 16
+    # two sequences: one-slice workgroups would need two rounds, two-slice ones fit
+    i = ops.prefill_launch_info([4096, 4096], compute_units=256, **kw)
+    assert (i["carry_kind"], i["slices_per_workgroup"], i["workgroups"]) == (0, 2, 256)
+    assert i["threads"] == 64 * 6
+    # the eight varlen sequences: throughput bound, four slices per workgroup
+    i = ops.prefill_launch_info([512, 1024, 2048, 3072, 4096, 5120, 6144, 8192],
+                                compute_units=256, **kw)
+    assert (i["carry_kind"], i["slices_per_workgroup"]) == (1, 4)
+    assert i["workgroups"] == 256 * 2 and i["threads"] == 64 * 6
+    assert i["prep_workgroups"] == sum((n + 63) // 64 for n in
+                                       (512, 1024, 2048, 3072, 4096, 5120, 6144, 8192)) * 16
+    # the same single sequence on a device with fewer CUs takes the two-slice split
+    i = ops.prefill_launch_info([4096], compute_units=200, **kw)
+    assert (i["carry_kind"], i["slices_per_workgroup"]) == (0, 2)
+    # workgroups of one head share blockIdx % 8 (one XCD): groups padded to 8
+    i = ops.prefill_launch_info([100] * 3, Hk=2, Hv=4, dk=128, dv=128, compute_units=256)
+    assert i["workgroups"] == 16 * 8  # 12 groups -> 16, eight slices each
+
+
+def test_prefill_launch_info_validates_like_the_entry_point():
+    kw = dict(Hk=16, Hv=32, dk=128, dv=128, compute_units=256)
+    with pytest.raises(ops.GdnError) as e:
+        ops.prefill_launch_info([10, 20], **dict(kw, Hk=5))
+    assert e.value.status == SHAPE
+    with pytest.raises(ops.GdnError) as e:
+        ops.prefill_launch_info([10, 20], **dict(kw, compute_units=0))
+    assert e.value.status == SHAPE

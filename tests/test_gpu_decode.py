@@ -351,3 +351,52 @@ def test_multi_token_verify_decode_b64(T):
     assert maxabs(f64(out).reshape(y.shape), y) <= TOL
     assert maxabs(f64(W["state_d"]), S) <= TOL
     assert maxabs(f64(W["conv_state_d"]), cs) == 0.0
+
+
+# ------------------------------------------------------------------ the ferrox-core device-step shapes
+
+def within_device_step_bound(a, b):
+    """The ferrox-core device-step test's bound, |a - b| <= 2e-4 max(|b|, 1), element
+    by element (checked beside this contract's 1e-3 max-abs)."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return bool(np.all(np.abs(a - b) <= 2e-4 * np.maximum(np.abs(b), 1.0)))
+
+
+@pytest.mark.parametrize("head_map", [synth.TILED, synth.GROUPED])
+def test_device_step_shapes_4_48_128(head_map):
+    """(n_k, n_v, S) = (4, 48, 128), tiled and grouped (a 12:1 head map), one token
+    of one sequence with the ferrox-core test's LCG draws: un-normalised uniform q
+    and k, g = -|u|, beta = 0.5 + 0.25 u, state uniform in [-0.5, 0.5), no L2 norm,
+    given gates, the core output (ferrox-core gdn.rs,
+    `the_device_delta_step_matches_this_one`)."""
+    n_k, n_v, s = 4, 48, 128
+    W = synth.device_step(n_k, n_v, s)
+    state = W["state"].unsqueeze(0).to(DEV).contiguous()
+    out = ops.decode_step(W["q"].reshape(1, -1).to(DEV), W["k"].reshape(1, -1).to(DEV),
+                          W["v"].reshape(1, -1).to(DEV), state, Hk=n_k, Hv=n_v, dk=s, dv=s,
+                          head_map=head_map, batch=1, g=W["g"].to(DEV), beta=W["beta"].to(DEV),
+                          l2norm_qk=False)
+    torch.cuda.synchronize()
+    y, S = oracle.core(f64(W["q"]), f64(W["k"]), f64(W["v"]), f64(W["state"]), head_map,
+                       g=f64(W["g"]), beta=f64(W["beta"]), l2norm_qk=False)
+    o = f64(out).reshape(y.shape)
+    assert np.max(np.abs(y)) > 1.0  # un-normalised keys: outputs well above 1
+    assert maxabs(o, y) <= TOL and maxabs(f64(state[0]), S) <= TOL
+    assert within_device_step_bound(o, y) and within_device_step_bound(f64(state[0]), S)
+
+
+def test_device_step_d4_is_not_built():
+    """The ferrox-core test's third shape, (2, 2, 4), has 4-wide heads, which no
+    kernel here is built for: the call is refused, and the oracle alone covers
+    d = 4 (exact-rational and hand-worked pins)."""
+    W = synth.device_step(2, 2, 4)
+    state = W["state"].unsqueeze(0).to(DEV).contiguous()
+    before = state.clone()
+    with pytest.raises(ops.GdnError) as e:
+        ops.decode_step(W["q"].reshape(1, -1).to(DEV), W["k"].reshape(1, -1).to(DEV),
+                        W["v"].reshape(1, -1).to(DEV), state, Hk=2, Hv=2, dk=4, dv=4,
+                        head_map=synth.TILED, batch=1, g=W["g"].to(DEV), beta=W["beta"].to(DEV),
+                        l2norm_qk=False)
+    assert e.value.status == 3  # GDN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(state, before)

@@ -210,3 +210,81 @@ def test_stream_state_hint_is_bitwise_neutral(T):
     assert maxabs(f64(res[1][0]).reshape(y.shape), y) <= TOL
     assert maxabs(f64(res[1][1]), S) <= TOL
     assert maxabs(f64(res[1][2]), cs) == 0.0
+
+
+# ------------------------------------------------------------------ the ferrox-core device-step shapes
+
+@pytest.mark.parametrize("head_map", [synth.TILED, synth.GROUPED])
+def test_fused_layer_device_step_shapes_4_48_128(head_map):
+    """The ferrox-core device-step shapes (4, 48, 128) through the one-launch layer.
+    The layer convolves its inputs first, so the LCG draws are its pre-conv rows,
+    and the taps (scale 0.5) and the window (scale 1) continue the same stream. No
+    L2 norm, given gates, the core output; the oracle runs its conv, the split and
+    the core in turn."""
+    from test_gpu_decode import within_device_step_bound
+    import oracle
+    n_k, n_v, s = 4, 48, 128
+    W = synth.device_step(n_k, n_v, s)
+    QK, QKV = n_k * s, 2 * n_k * s + n_v * s
+    x = torch.cat([W["q"].reshape(1, -1), W["k"].reshape(1, -1), W["v"].reshape(1, -1)], 1)
+    conv_w = torch.from_numpy(W["rng"].draw(QKV * 4, 0.5).reshape(QKV, 4))
+    window = torch.from_numpy(W["rng"].draw(QKV * 3, 1.0).reshape(1, QKV, 3))
+    xd = x.to(DEV).contiguous()
+    state = W["state"].unsqueeze(0).to(DEV).contiguous()
+    cs_in, cs_out = window.to(DEV), torch.empty_like(window, device=DEV)
+    out = ops.decode_layer(xd[:, :QK], xd[:, QK:2 * QK], xd[:, 2 * QK:], state, conv_w.to(DEV),
+                           cs_in, cs_out, Hk=n_k, Hv=n_v, dk=s, dv=s, head_map=head_map, batch=1,
+                           g=W["g"].to(DEV), beta=W["beta"].to(DEV), l2norm_qk=False)
+    torch.cuda.synchronize()
+    ycv, cs = oracle.conv(f64(x), f64(conv_w), f64(window[0]))
+    q = ycv[:, :QK].reshape(1, n_k, s)
+    k = ycv[:, QK:2 * QK].reshape(1, n_k, s)
+    v = ycv[:, 2 * QK:].reshape(1, n_v, s)
+    y, S = oracle.core(q, k, v, f64(W["state"]), head_map, g=f64(W["g"]), beta=f64(W["beta"]),
+                       l2norm_qk=False)
+    o = f64(out).reshape(y.shape)
+    assert maxabs(o, y) <= TOL and maxabs(f64(state[0]), S) <= TOL
+    assert within_device_step_bound(o, y) and within_device_step_bound(f64(state[0]), S)
+    assert maxabs(f64(cs_out[0]), cs) == 0.0
+
+
+# ------------------------------------------------------------------ slot pools across calls
+
+def test_pool_slot_sits_out_a_step_and_rejoins():
+    """Three pooled sequences over three steps with alternating conv buffers; slot 1
+    sits out the middle step. The caller carries that slot's window into the buffer
+    the next call reads (the contract gdn.h states for pools), and every output,
+    state and window then matches the oracle run per sequence. Without the carry
+    the buffer would hold the slot's stale window, which the test also shows."""
+    Hk, Hv, d, nslots = 2, 4, 64, 3
+    W = to_dev(synth.decode_batch(seed=71, B=nslots, Hk=Hk, Hv=Hv, dk=d, dv=d))
+    pool, bufs = W["state_d"], [W["conv_state_d"].clone(), torch.zeros_like(W["conv_state_d"])]
+    S_ref = {s: f64(W["state"][s:s + 1]) for s in range(nslots)}
+    cs_ref = {s: f64(W["conv_state"][s:s + 1]) for s in range(nslots)}
+    schedule = [[0, 1, 2], [2, 0], [1, 0, 2]]
+    par = 0
+    for step, slots in enumerate(schedule):
+        Ws = synth.decode_batch(seed=700 + step, B=len(slots), Hk=Hk, Hv=Hv, dk=d, dv=d)
+        Ws = to_dev(dict(Ws, conv_w=W["conv_w"], A_log=W["A_log"]))
+        cs_in, cs_out = bufs[par], bufs[1 - par]
+        out = run_fused(Ws, T=1, B=len(slots), cs_in=cs_in, cs_out=cs_out, state=pool,
+                        slots=torch.tensor(slots, dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        for bi, s in enumerate(slots):
+            Wi = dict(Ws)
+            for key in ("x", "z", "a", "b"):
+                Wi[key] = Ws[key][bi:bi + 1]
+            y, cs_ref[s], S_ref[s] = oracle_layer(Wi, B=1, T=1, state=S_ref[s],
+                                                 conv_state=cs_ref[s])
+            assert maxabs(f64(out[bi:bi + 1]).reshape(y.shape), y) <= TOL, f"step {step} slot {s}"
+        left_out = [s for s in range(nslots) if s not in slots]
+        for s in left_out:
+            # the slot's latest window is in the buffer this call read; the one the
+            # next call reads holds an older one until the caller carries it over
+            assert not torch.equal(cs_out[s], cs_in[s])
+            cs_out[s].copy_(cs_in[s])
+        par = 1 - par
+    torch.cuda.synchronize()
+    for s in range(nslots):
+        assert maxabs(f64(pool[s]), S_ref[s][0]) <= TOL
+        assert maxabs(f64(bufs[par][s]), cs_ref[s][0]) == 0.0

@@ -11,17 +11,18 @@ import torch
 
 import oracle
 from gated_deltanet_linear_step_amd import ops, synth
-from helpers import f64, maxabs, oracle_core_heads, ulp16
+from helpers import f64, maxabs, oracle_core_heads, threads, ulp16
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 TOL_OUT, TOL_STATE = 0.012, 1e-3
+TOL_DECODE = 1e-3  # decode outputs and states
 
 
 def run_prefill(P, *, state=None, out_dtype=torch.float32, raw=True, gated=False, lo=None, hi=None,
-                cu=None):
+                cu=None, decay=ops.DECAY_LOG_RATE, l2norm_qk=True):
     """Prefill over P's packed tokens [lo, hi) (default: all) with cu_seqlens cu."""
-    Hk, Hv, d = P["Hk"], P["Hv"], P["dk"]
+    Hk, Hv, dk, dv_ = P["Hk"], P["Hv"], P["dk"], P["dv"]
     lo = 0 if lo is None else lo
     hi = P["q"].shape[0] if hi is None else hi
     cu = P["cu_seqlens"] if cu is None else cu
@@ -29,24 +30,26 @@ def run_prefill(P, *, state=None, out_dtype=torch.float32, raw=True, gated=False
     kw = {}
     if raw:
         kw.update(a=dv(P["a"]), b=dv(P["b"]), decay_param=P["A_log"].to(DEV),
-                  dt_bias=P["dt_bias"].to(DEV))
+                  dt_bias=P["dt_bias"].to(DEV), decay=decay)
     else:
         kw.update(g=dv(P["g"]), beta=dv(P["beta"]))
     if gated:
         kw.update(z=P["z"][lo:hi].to(DEV).contiguous(), norm_weight=P["norm_w"].to(DEV))
     st = P["state"].to(DEV).contiguous() if state is None else state
-    out = ops.prefill_chunked(dv(P["q"]), dv(P["k"]), dv(P["v"]), st, cu, Hk=Hk, Hv=Hv, dk=d,
-                              dv=d, head_map=P["head_map"], out_dtype=out_dtype, **kw)
+    out = ops.prefill_chunked(dv(P["q"]), dv(P["k"]), dv(P["v"]), st, cu, Hk=Hk, Hv=Hv, dk=dk,
+                              dv=dv_, head_map=P["head_map"], out_dtype=out_dtype,
+                              l2norm_qk=l2norm_qk, **kw)
     return out, st
 
 
-def oracle_seq(P, i, S0, heads=None, raw=True, gated=False):
+def oracle_seq(P, i, S0, heads=None, raw=True, gated=False, decay=ops.DECAY_LOG_RATE,
+               l2norm_qk=True):
     cu = P["cu_seqlens"]
     lo, hi = int(cu[i]), int(cu[i + 1])
-    kw = {}
+    kw = dict(l2norm_qk=l2norm_qk)
     if raw:
         kw.update(a=f64(P["a"][lo:hi]), b=f64(P["b"][lo:hi]), decay_param=f64(P["A_log"]),
-                  dt_bias=f64(P["dt_bias"]))
+                  dt_bias=f64(P["dt_bias"]), decay_kind=decay)
     else:
         kw.update(g=f64(P["g"][lo:hi]), beta=f64(P["beta"][lo:hi]))
     if gated:
@@ -54,6 +57,28 @@ def oracle_seq(P, i, S0, heads=None, raw=True, gated=False):
     heads = range(P["Hv"]) if heads is None else heads
     return oracle_core_heads(f64(P["q"][lo:hi]), f64(P["k"][lo:hi]), f64(P["v"][lo:hi]), S0,
                              P["head_map"], heads, **kw)
+
+
+def split_with_sentinel(P, split, **kw):
+    """The whole sequence in one call and in two calls split at a token that is not
+    chunk-aligned, each on a state with sentinels on both sides. Returns the two
+    outputs and the two final states; asserts that no sentinel moved."""
+    T = P["q"].shape[0]
+    Hv, dv, dk = P["Hv"], P["dv"], P["dk"]
+    n = Hv * dv * dk
+    states = []
+    for _ in range(2):
+        guard = torch.full((n + 32,), 73.25, device=DEV)
+        guard[16:16 + n] = P["state"].reshape(-1).to(DEV)
+        states.append((guard, guard[16:16 + n].view(1, Hv, dv, dk)))
+    out, _ = run_prefill(P, state=states[0][1], **kw)
+    o1, _ = run_prefill(P, state=states[1][1], lo=0, hi=split, cu=synth.cu_seqlens([split]), **kw)
+    o2, _ = run_prefill(P, state=states[1][1], lo=split, hi=T, cu=synth.cu_seqlens([T - split]),
+                        **kw)
+    torch.cuda.synchronize()
+    for guard, _ in states:
+        assert torch.all(guard[:16] == 73.25) and torch.all(guard[16 + n:] == 73.25)
+    return out, torch.cat([o1, o2]), states[0][1], states[1][1]
 
 
 # ------------------------------------------------------------------ the chunk-core workload
@@ -95,6 +120,113 @@ def test_chunk_core_145_tokens_split_73_with_sentinel(Hk, Hv, head_map):
     assert maxabs(f64(st2), f64(st)) <= TOL_STATE
 
 
+# ------------------------------------------------------------------ decay and normalisation variants
+
+@pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
+def test_negative_rate_decay_145_tokens_split_73_with_sentinel(head_map):
+    """GDN_DECAY_NEGATIVE_RATE through the prefill: the rate multiplying softplus is
+    passed as is (the ferrum-kernels tests page's NegativeRate parameterisation)."""
+    P = synth.prefill(seed=41, lengths=[145], Hk=2, Hv=4, head_map=head_map, state_std=0.05)
+    P["A_log"] = synth.negative_rates(41, P["Hv"])  # the decay parameter, here a rate
+    dec = ops.DECAY_NEGATIVE_RATE
+    out, out_split, st, st_split = split_with_sentinel(P, 73, decay=dec)
+    y, S = oracle_seq(P, 0, f64(P["state"][0]), decay=dec)
+    assert np.any(np.abs(f64(out)) > 1e-3)
+    assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(out_split), y) <= TOL_OUT
+    assert maxabs(f64(st[0]), S) <= TOL_STATE and maxabs(f64(st_split[0]), S) <= TOL_STATE
+    # the same rates given as A_log = log(-rate) under the log-rate form agree
+    yl, Sl = oracle_seq(dict(P, A_log=torch.log(-P["A_log"].double())), 0, f64(P["state"][0]))
+    assert maxabs(yl, y) <= 1e-9 and maxabs(Sl, S) <= 1e-9
+
+
+@pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
+def test_unnormalised_qk_145_tokens_split_73_with_sentinel(head_map):
+    """No in-op L2 norm: the ferrox-core generator's un-normalised uniform q and k
+    (scaled so |k|^2 stays near 1 and the rule is stable), given g and beta."""
+    P = synth.lcg_prefill(T=145, Hk=2, Hv=4, dk=128, dv=128)
+    P["head_map"] = head_map
+    out, out_split, st, st_split = split_with_sentinel(P, 73, raw=False, l2norm_qk=False)
+    y, S = oracle_seq(P, 0, f64(P["state"][0]), raw=False, l2norm_qk=False)
+    assert np.any(np.abs(f64(out)) > 1e-2)
+    assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(out_split), y) <= TOL_OUT
+    assert maxabs(f64(st[0]), S) <= TOL_STATE and maxabs(f64(st_split[0]), S) <= TOL_STATE
+
+
+@pytest.mark.parametrize("nseq,Hv", [(1, 2), (12, 4), (24, 4)])
+def test_zero_beta_decays_the_state_by_the_summed_gates(nseq, Hv):
+    """beta = 0 writes nothing, so after T tokens of weak decay the state is exactly
+    exp(sum g) S0 and o_t = scale exp(G_t) S0 q_t (closed forms of the rule). The
+    state check is tight (1e-5 on |S0| <= 0.5): a decay factor taken from the
+    wrong token of a chunk is off by several percent. Sequence and head counts
+    select the three carry shapes (one-slice split, two-slice split, four-slice)."""
+    lengths = [200 - 7 * i for i in range(nseq)]  # 3 full chunks + a partial one, ragged
+    T, Hk, d = sum(lengths), 1, 128
+    r = synth.Lcg(91)
+    P = dict(Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, cu_seqlens=synth.cu_seqlens(lengths),
+             state=torch.from_numpy(r.draw(nseq * Hv * d * d, 0.5).reshape(nseq, Hv, d, d)),
+             q=torch.from_numpy(r.draw(T * Hk * d, 1.0).reshape(T, Hk, d)),
+             k=torch.from_numpy(r.draw(T * Hk * d, 1.0).reshape(T, Hk, d)),
+             v=torch.from_numpy(r.draw(T * Hv * d, 1.0).reshape(T, Hv, d)),
+             g=torch.from_numpy((np.float32(-0.05) * np.abs(r.draw(T * Hv, 1.0))).reshape(T, Hv)),
+             beta=torch.zeros(T, Hv))
+    groups = nseq * Hv
+    info = ops.prefill_launch_info(lengths, Hk=Hk, Hv=Hv, dk=d, dv=d, compute_units=256,
+                                   head_map=synth.TILED, flags=ops.L2NORM_QK)
+    assert (info["carry_kind"], info["slices_per_workgroup"]) == \
+        ((0, 1) if groups <= 32 else (0, 2) if groups <= 64 else (1, 4))
+    out, st = run_prefill(P, raw=False)
+    torch.cuda.synchronize()
+    cu = P["cu_seqlens"].tolist()
+    g = f64(P["g"])
+    qn = f64(P["q"]) / np.linalg.norm(f64(P["q"]), axis=-1, keepdims=True)
+    for i in range(nseq):
+        G = np.cumsum(g[cu[i]:cu[i + 1]], axis=0)  # [t][h]
+        S0 = f64(P["state"][i])
+        S_exact = np.exp(G[-1])[:, None, None] * S0
+        assert np.max(np.abs(f64(st[i]) - S_exact)) <= 1e-5, f"seq {i} state"
+        o_exact = np.exp(G)[:, :, None] * np.einsum("hji,ti->thj", S0, qn[cu[i]:cu[i + 1], 0]) / \
+            np.sqrt(d)
+        assert maxabs(f64(out[cu[i]:cu[i + 1]]), o_exact) <= TOL_OUT, f"seq {i} out"
+
+
+def test_int64_cu_seqlens_through_the_binding():
+    """A torch int64 cu_seqlens (torch's default integer type) reaches the kernels as
+    the int32 [N+1] array they read, on the device as on the host."""
+    lengths = [70, 0, 129]
+    P = synth.prefill(seed=42, lengths=lengths, Hk=2, Hv=4, head_map=synth.TILED, state_std=0.05)
+    cu64 = P["cu_seqlens"].to(torch.int64)
+    o_dev, s_dev = run_prefill(P, cu=cu64.to(DEV))
+    o_host, s_host = run_prefill(P, cu=cu64)
+    o_ref, s_ref = run_prefill(P)
+    torch.cuda.synchronize()
+    assert torch.equal(o_dev, o_ref) and torch.equal(s_dev, s_ref)
+    assert torch.equal(o_host, o_ref) and torch.equal(s_host, s_ref)
+    y, S = oracle.packed(f64(P["q"]), f64(P["k"]), f64(P["v"]), f64(P["state"]), P["head_map"],
+                         P["cu_seqlens"], a=f64(P["a"]), b=f64(P["b"]),
+                         decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]), nthreads=4)
+    assert maxabs(f64(o_ref), y) <= TOL_OUT and maxabs(f64(s_ref), S) <= TOL_STATE
+
+
+def test_binding_rejects_misshaped_buffers_before_any_launch():
+    P = synth.prefill(seed=43, lengths=[10, 20], Hk=2, Hv=4, head_map=synth.TILED,
+                      state_std=0.02)
+    st = P["state"].to(DEV)
+    before = st.clone()
+    with pytest.raises(ValueError):  # state of another head shape
+        run_prefill(P, state=st.view(2, 4, 64, 256))
+    with pytest.raises(ValueError):  # fewer state slots than sequences
+        run_prefill(P, state=st[:1].contiguous())
+    with pytest.raises(TypeError):  # offsets as floats
+        run_prefill(P, state=st, cu=P["cu_seqlens"].float())
+    with pytest.raises(ValueError):  # an output too small for the tokens
+        ops.prefill_chunked(*(P[x][:30].reshape(30, -1).to(DEV) for x in ("q", "k", "v")), st,
+                            P["cu_seqlens"], Hk=2, Hv=4, dk=128, dv=128, head_map=synth.TILED,
+                            g=torch.zeros(30, 4, device=DEV), beta=torch.zeros(30, 4, device=DEV),
+                            out=torch.empty(29, 4, 128, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(st, before)
+
+
 # ------------------------------------------------------------------ single long sequence (T=4096)
 
 def test_prefill_t4096_grouped_bf16_matches_oracle():
@@ -109,39 +241,45 @@ def test_prefill_t4096_grouped_bf16_matches_oracle():
 # ------------------------------------------------------------------ varlen prefill then decode
 
 def test_varlen_prefill_then_64_decode_steps():
+    """The packed eight-sequence prefill (512..8192 tokens, tiled, nonzero initial
+    states), then 64 batched decode steps with fresh inputs. Every output of every
+    v-head and every final state is compared with the token-by-token oracle:
+    (A) the whole pipeline at the prefill tolerances, the GPU's state carried from
+    the prefill into the decode; (B) the decode steps from the oracle's own
+    post-prefill state (rounded to f32) at the decode tolerances."""
     lengths = [512, 1024, 2048, 3072, 4096, 5120, 6144, 8192]
     P = synth.prefill(seed=5, lengths=lengths, head_map=synth.TILED, state_std=0.02)
     Hk, Hv, d = P["Hk"], P["Hv"], P["dk"]
     out, st = run_prefill(P)
     torch.cuda.synchronize()
-    heads = [0, 13, 31]  # sampled v-heads, all sequences, every token
-    S_ref = {}
+    y, S = oracle.packed(f64(P["q"]), f64(P["k"]), f64(P["v"]), f64(P["state"]), synth.TILED,
+                         P["cu_seqlens"], a=f64(P["a"]), b=f64(P["b"]),
+                         decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]),
+                         nthreads=threads())
     for i in range(len(lengths)):
         lo, hi = int(P["cu_seqlens"][i]), int(P["cu_seqlens"][i + 1])
-        y, S = oracle_seq(P, i, f64(P["state"][i]), heads=heads)
-        assert maxabs(f64(out[lo:hi, heads]), y[:, heads]) <= TOL_OUT, f"seq {i} out"
-        assert maxabs(f64(st[i, heads]), S[heads]) <= TOL_STATE, f"seq {i} state"
-        S_ref[i] = S
-    # 64 batched decode steps (B=8) with fresh inputs, the state carried on both sides
+        assert maxabs(f64(out[lo:hi]), y[lo:hi]) <= TOL_OUT, f"seq {i} out"
+        assert maxabs(f64(st[i]), S[i]) <= TOL_STATE, f"seq {i} state"
+    stB = torch.from_numpy(S).float().to(DEV)  # (B): the oracle's state, in f32
+    S_A, S_B = S, f64(stB)
+    common = dict(Hk=Hk, Hv=Hv, dk=d, dv=d, head_map=synth.TILED, batch=8,
+                  decay_param=P["A_log"].to(DEV), dt_bias=P["dt_bias"].to(DEV))
     for step in range(64):
         D = synth.prefill(seed=5000 + step, lengths=[1] * 8, head_map=synth.TILED)
-        o = ops.decode_step(D["q"].reshape(8, -1).to(DEV), D["k"].reshape(8, -1).to(DEV),
-                            D["v"].reshape(8, -1).to(DEV), st, Hk=Hk, Hv=Hv, dk=d, dv=d,
-                            head_map=synth.TILED, batch=8, a=D["a"].to(DEV), b=D["b"].to(DEV),
-                            decay_param=P["A_log"].to(DEV), dt_bias=P["dt_bias"].to(DEV))
-        if step in (0, 63):
-            torch.cuda.synchronize()
-        for i in range(8):
-            yo, So = oracle.core(f64(D["q"][i:i + 1]), f64(D["k"][i:i + 1]),
-                                 f64(D["v"][i:i + 1]), S_ref[i], synth.TILED,
-                                 a=f64(D["a"][i:i + 1]), b=f64(D["b"][i:i + 1]),
-                                 decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]),
-                                 heads=(heads[0], heads[-1] + 1))
-            S_ref[i] = So
-            if step in (0, 63):
-                assert maxabs(f64(o[i, heads]), yo[0, heads]) <= TOL_OUT
-    for i in range(8):
-        assert maxabs(f64(st[i, heads]), S_ref[i][heads]) <= TOL_STATE
+        args = [D[x].reshape(8, -1).to(DEV) for x in ("q", "k", "v")]
+        gates = dict(a=D["a"].to(DEV), b=D["b"].to(DEV))
+        oA = ops.decode_step(*args, st, **common, **gates)
+        oB = ops.decode_step(*args, stB, **common, **gates)
+        torch.cuda.synchronize()
+        kw = dict(a=f64(D["a"]), b=f64(D["b"]), decay_param=f64(P["A_log"]),
+                  dt_bias=f64(P["dt_bias"]), nthreads=8)
+        cu1 = np.arange(9)
+        yA, S_A = oracle.packed(f64(D["q"]), f64(D["k"]), f64(D["v"]), S_A, synth.TILED, cu1, **kw)
+        yB, S_B = oracle.packed(f64(D["q"]), f64(D["k"]), f64(D["v"]), S_B, synth.TILED, cu1, **kw)
+        assert maxabs(f64(oA), yA) <= TOL_OUT, f"step {step} (A)"
+        assert maxabs(f64(oB), yB) <= TOL_DECODE, f"step {step} (B)"
+    assert maxabs(f64(st), S_A) <= TOL_STATE
+    assert maxabs(f64(stB), S_B) <= TOL_DECODE
 
 
 # ------------------------------------------------------------------ edges, dtypes, gated norm

@@ -449,3 +449,39 @@ def test_core_given_gates_equals_recurrence():
     y, S = oracle.core(q, k, v, S0, oracle.MAP_TILED, g=g, beta=beta, l2norm_qk=False)
     o, S2 = oracle.recurrence(q, k, v, g, beta, S0, oracle.MAP_TILED)
     assert np.array_equal(y, o) and np.array_equal(S, S2)
+
+
+@pytest.mark.parametrize("head_map", ["grouped", "tiled"])
+@pytest.mark.parametrize("raw", [True, False])
+def test_packed_driver_equals_per_sequence_core(head_map, raw):
+    """oracle.packed (one (sequence, v-head) pair per call, spread over threads) adds
+    no arithmetic: it equals core over each whole sequence bit for bit, empty
+    sequences leave their states alone, and a v-head subset leaves the rest."""
+    rng = np.random.default_rng(31)
+    Hk, Hv, dk, dv = 2, 6, 8, 4
+    lengths = [5, 0, 3, 7]
+    T, N = sum(lengths), len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k = rng.normal(size=(T, Hk, dk)), rng.normal(size=(T, Hk, dk))
+    v, z = rng.normal(size=(T, Hv, dv)), rng.normal(size=(T, Hv, dv))
+    S0 = rng.normal(0, 0.1, size=(N, Hv, dv, dk))
+    kw = dict(z=z, norm_w=rng.normal(size=dv))
+    if raw:
+        kw.update(a=rng.normal(size=(T, Hv)), b=rng.normal(size=(T, Hv)),
+                  decay_param=rng.uniform(-2, 0, Hv), dt_bias=rng.normal(size=Hv))
+    else:
+        kw.update(g=-rng.uniform(0, 0.5, (T, Hv)), beta=rng.uniform(0, 1, (T, Hv)))
+    y, S = oracle.packed(q, k, v, S0, MAPS[head_map], cu, nthreads=3, **kw)
+    for i in range(N):
+        lo, hi = cu[i], cu[i + 1]
+        if lo == hi:
+            assert np.array_equal(S[i], S0[i])
+            continue
+        seq = {key: (val[lo:hi] if key in ("a", "b", "g", "beta", "z") else val)
+               for key, val in kw.items()}
+        yi, Si = oracle.core(q[lo:hi], k[lo:hi], v[lo:hi], S0[i], MAPS[head_map], **seq)
+        assert np.array_equal(y[lo:hi], yi) and np.array_equal(S[i], Si)
+    ys, Ss = oracle.packed(q, k, v, S0, MAPS[head_map], cu, heads=[1, 4], **kw)
+    assert np.array_equal(ys[:, [1, 4]], y[:, [1, 4]]) and np.all(ys[:, [0, 2, 3, 5]] == 0)
+    assert np.array_equal(Ss[:, [1, 4]], S[:, [1, 4]])
+    assert np.array_equal(Ss[:, [0, 2, 3, 5]], S0[:, [0, 2, 3, 5]])
