@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "gdn_kernels.h"
 
@@ -141,6 +142,78 @@ gdn_status check_cu(const int32_t *cu, int32_t n, int32_t total, int64_t *chunks
     return GDN_OK;
 }
 
+// Everything gdn_prefill_chunked checks except the workspace; fills the kernel
+// parameters, the workspace the call needs, and whether it has no tokens at all.
+gdn_status prefill_prepare(const gdn_dims *dims, int32_t num_seqs, const int32_t *cu_seqlens_host,
+                           const int32_t *cu_seqlens_dev, int32_t total_tokens, const gdn_inputs *in,
+                           float *state, int32_t out_dtype, void *out, gdn::PrefillParams &p,
+                           size_t &need, bool &empty)
+{
+    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::prefill_supported, kPrefillFlags,
+                                 p.hc, p.in);
+    if (st != GDN_OK)
+        return st;
+    if (num_seqs < 0 || total_tokens < 0)
+        return GDN_ERR_SHAPE;
+    if (!cu_seqlens_host || !cu_seqlens_dev)
+        return GDN_ERR_NULL;
+    empty = total_tokens == 0;
+    if (num_seqs == 0)
+        return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    int64_t chunks = 0, max_chunks = 0;
+    st = check_cu(cu_seqlens_host, num_seqs, total_tokens, &chunks, &max_chunks);
+    if (st != GDN_OK)
+        return st;
+    if ((int64_t)total_tokens * dims->num_v_heads > kI32Max || chunks * dims->num_v_heads > kI32Max)
+        return GDN_ERR_OVERFLOW;
+    const int64_t mc = (int64_t)total_tokens / gdn::kChunk + num_seqs;
+    need = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim_k,
+                                        dims->head_dim_v, mc, num_seqs, total_tokens,
+                                        (dims->flags & GDN_GATED_NORM) != 0);
+    p.state = state;
+    p.out = out;
+    p.out_dt = out_dtype;
+    p.N = num_seqs;
+    p.total = total_tokens;
+    p.cu = cu_seqlens_dev;
+    p.num_chunks = (int)chunks;
+    p.max_seq_chunks = (int)max_chunks;
+    return GDN_OK;
+}
+
+// ---- the static scratch of gdn_prefill_chunked_noalloc ----------------------
+// The prefill's workspace for callers that cannot allocate (graph capture, tight
+// serving loops): a file-scope device array, one copy per GPU, held until the
+// process ends. In host code `scratch` names a host-side stand-in, never device
+// memory: its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void *g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void **addr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch[dev] = p;
+    }
+    *addr = g_scratch[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,6 +229,7 @@ const char *gdn_status_string(gdn_status s)
     case GDN_ERR_ALIGN: return "a pointer or stride is not aligned as required";
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+    case GDN_ERR_SCRATCH: return "the call needs more than the no-allocation entry point's static scratch";
     }
     return "unknown status";
 }
@@ -345,38 +419,40 @@ gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
                                size_t workspace_bytes, void *stream)
 {
     gdn::PrefillParams p{};
-    gdn_status st = check_common(dims, in, out_dtype, out, state, gdn::prefill_supported, kPrefillFlags,
-                                 p.hc, p.in);
-    if (st != GDN_OK)
+    size_t need = 0;
+    bool empty = false;
+    gdn_status st = prefill_prepare(dims, num_seqs, cu_seqlens_host, cu_seqlens_dev, total_tokens, in,
+                                    state, out_dtype, out, p, need, empty);
+    if (st != GDN_OK || (empty && num_seqs == 0))
         return st;
-    if (num_seqs < 0 || total_tokens < 0)
-        return GDN_ERR_SHAPE;
-    if (!cu_seqlens_host || !cu_seqlens_dev)
-        return GDN_ERR_NULL;
-    if (num_seqs == 0)
-        return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
-    int64_t chunks = 0, max_chunks = 0;
-    st = check_cu(cu_seqlens_host, num_seqs, total_tokens, &chunks, &max_chunks);
-    if (st != GDN_OK)
-        return st;
-    if ((int64_t)total_tokens * dims->num_v_heads > kI32Max || chunks * dims->num_v_heads > kI32Max)
-        return GDN_ERR_OVERFLOW;
-    const size_t need = gdn_prefill_workspace_bytes(dims, num_seqs, total_tokens);
     if (!workspace || workspace_bytes < need)
         return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256))
         return GDN_ERR_ALIGN;
-    if (total_tokens == 0)
+    if (empty)
         return GDN_OK;  // every sequence empty: states untouched
-    p.state = state;
-    p.out = out;
-    p.out_dt = out_dtype;
-    p.N = num_seqs;
-    p.total = total_tokens;
-    p.cu = cu_seqlens_dev;
-    p.num_chunks = (int)chunks;
-    p.max_seq_chunks = (int)max_chunks;
     gdn::prefill_carve(p, workspace, (int64_t)total_tokens / gdn::kChunk + num_seqs);
+    return launch_status(gdn::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_dims *dims, int32_t num_seqs,
+                                       const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                                       int32_t total_tokens, const gdn_inputs *in, float *state,
+                                       int32_t out_dtype, void *out, void *stream)
+{
+    gdn::PrefillParams p{};
+    size_t need = 0;
+    bool empty = false;
+    gdn_status st = prefill_prepare(dims, num_seqs, cu_seqlens_host, cu_seqlens_dev, total_tokens, in,
+                                    state, out_dtype, out, p, need, empty);
+    if (st != GDN_OK || empty)
+        return st;
+    if (need > kScratchBytes)
+        return GDN_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess)
+        return GDN_ERR_LAUNCH;
+    gdn::prefill_carve(p, ws, (int64_t)total_tokens / gdn::kChunk + num_seqs);
     return launch_status(gdn::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("GDN_LIB_PATH") or os.path.join(HERE, "libgdn.so")
 GDN_OK = 0
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
                 4: "GDN_ERR_OVERFLOW", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_WORKSPACE",
-                7: "GDN_ERR_LAUNCH"}
+                7: "GDN_ERR_LAUNCH", 8: "GDN_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 F32, F16, BF16 = 0, 1, 2
 MAP_GROUPED, MAP_TILED = 0, 1
 DECAY_LOG_RATE, DECAY_NEGATIVE_RATE = 0, 1
@@ -28,7 +29,7 @@ CHUNK = 64
 
 EXPORTED = ["gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
             "gdn_prefill_chunked", "gdn_status_string", "gdn_version", "gdn_decode_layer",
-            "gdn_decode_launch_info", "gdn_prefill_launch_info"]
+            "gdn_decode_launch_info", "gdn_prefill_launch_info", "gdn_prefill_chunked_noalloc"]
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _VP = ctypes.c_void_p
@@ -107,6 +108,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill_chunked.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _VP, _VP,
                                         ctypes.c_int32, ctypes.POINTER(Inputs), _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _VP, _VP,
+                                                ctypes.c_int32, ctypes.POINTER(Inputs), _VP,
+                                                ctypes.c_int32, _VP, _VP]
     lib.gdn_decode_launch_info.restype = ctypes.c_int
     lib.gdn_decode_launch_info.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.POINTER(LaunchInfo)]
@@ -420,6 +425,37 @@ def prefill_chunked(q, k, v, state, cu_seqlens, *, Hk, Hv, dk, dv, head_map, a=N
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream))
     _check(st, "gdn_prefill_chunked")
+    del keep
+    return out
+
+
+def prefill_chunked_noalloc(q, k, v, state, cu_seqlens, out, *, cu_seqlens_host, Hk, Hv, dk, dv,
+                            head_map, a=None, b=None, decay_param=None, dt_bias=None, g=None,
+                            beta=None, z=None, norm_weight=None, l2norm_qk=True,
+                            decay=DECAY_LOG_RATE, scale=0.0, stream=None):
+    """One call of gdn_prefill_chunked_noalloc: the prefill with the library's static
+    scratch as its workspace. The caller passes every buffer, out included, and the
+    offsets on both sides (int32 [N+1] on the GPU and on the host), so the binding
+    itself allocates nothing. Returns out."""
+    flags = (L2NORM_QK if l2norm_qk else 0) | (RAW_GATES if a is not None else 0) | \
+        (GATED_NORM if z is not None else 0)
+    dims = make_dims(Hk, Hv, dk, dv, head_map, flags, decay, scale)
+    inp, keep = make_inputs(q, k, v, Hk=Hk, Hv=Hv, dk=dk, dv=dv, a=a, b=b,
+                            decay_param=decay_param, dt_bias=dt_bias, g=g, beta=beta, z=z,
+                            norm_weight=norm_weight)
+    for name, t, dev in (("cu_seqlens", cu_seqlens, True), ("cu_seqlens_host", cu_seqlens_host, False)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.is_cuda != dev:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on the "
+                             f"{'GPU' if dev else 'host'}")
+    N = cu_seqlens_host.numel() - 1
+    total = int(cu_seqlens_host[-1])
+    _check_state(state, Hv, dv, dk)
+    _check_out(out, total, Hv, dv)
+    st = load().gdn_prefill_chunked_noalloc(ctypes.byref(dims), N,
+                                            ctypes.c_void_p(cu_seqlens_host.data_ptr()),
+                                            _ptr(cu_seqlens), total, ctypes.byref(inp),
+                                            _ptr(state), _dt(out), _ptr(out), _stream(stream))
+    _check(st, "gdn_prefill_chunked_noalloc")
     del keep
     return out
 

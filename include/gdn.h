@@ -46,7 +46,9 @@ typedef enum gdn_status {
     GDN_ERR_OVERFLOW = 4,    /* an element count or offset exceeds what the kernels index */
     GDN_ERR_ALIGN = 5,       /* a pointer or stride breaks the alignment a kernel needs */
     GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query returned */
-    GDN_ERR_LAUNCH = 7       /* the HIP runtime reported an error for a launch */
+    GDN_ERR_LAUNCH = 7,      /* the HIP runtime reported an error for a launch */
+    GDN_ERR_SCRATCH = 8      /* gdn_prefill_chunked_noalloc: the call needs more workspace
+                                than its static scratch (GDN_NOALLOC_SCRATCH_BYTES) */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
@@ -261,6 +263,30 @@ gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
                                int32_t total_tokens, const gdn_inputs *in, float *state,
                                int32_t out_dtype, void *out, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * gdn_prefill_chunked_noalloc -- gdn_prefill_chunked for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * workspace in a static device array of the library instead of a caller buffer.
+ *
+ * Arguments and errors are those of gdn_prefill_chunked without the workspace.
+ * The call allocates nothing. The array holds GDN_NOALLOC_SCRATCH_BYTES per GPU
+ * (64 MiB: about 1,700 tokens of one sequence at Hk=16, Hv=32, dk=dv=128 without
+ * the gated norm); a call whose gdn_prefill_workspace_bytes exceeds it returns
+ * GDN_ERR_SCRATCH and launches nothing. Each GPU the library runs on holds its
+ * own copy of the array until the process ends (its device address is looked
+ * up on the first call on that device). Every call on one GPU shares that GPU's
+ * copy and leaves its contents behind; nothing in it needs to start at zero.
+ * Calls that overlap in time on one GPU (different streams, or different host
+ * threads without ordering) race on the array: order them.
+ * ------------------------------------------------------------------------- */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_chunked_noalloc(const gdn_dims *dims, int32_t num_seqs,
+                                       const int32_t *cu_seqlens_host,
+                                       const int32_t *cu_seqlens_dev, int32_t total_tokens,
+                                       const gdn_inputs *in, float *state, int32_t out_dtype,
+                                       void *out, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Kernel selection, for inspection and host-side tests. Which kernel a call runs

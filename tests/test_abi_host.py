@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = ops.load()
-    for s in range(8):
+    for s in range(9):
         assert len(ops.status_string(s)) > 0
     assert ops.status_string(99) == "unknown status"
     assert lib.gdn_version() >= 100
@@ -285,3 +285,30 @@ def test_prefill_launch_info_validates_like_the_entry_point():
     with pytest.raises(ops.GdnError) as e:
         ops.prefill_launch_info([10, 20], **dict(kw, compute_units=0))
     assert e.value.status == SHAPE
+
+
+def test_noalloc_prefill_rejects_what_its_scratch_cannot_hold():
+    """gdn_prefill_chunked_noalloc validates like gdn_prefill_chunked and refuses a call
+    whose workspace would exceed its static scratch, before any HIP call."""
+    lib = ops.load()
+    d = dims(head_map=ops.MAP_GROUPED)
+    Hk, Hv = 16, 32
+    big = dims(Hk=Hk, Hv=Hv, head_map=ops.MAP_GROUPED)
+    T = 4096
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(big), 1, T) > ops.NOALLOC_SCRATCH_BYTES
+    cu = (ctypes.c_int32 * 2)(0, T)
+
+    def call(dd, cu_h, total, N):
+        return lib.gdn_prefill_chunked_noalloc(ctypes.byref(dd), N, cu_h, vp(P16), total,
+                                               ctypes.byref(inputs(q_stride=4096, k_stride=4096,
+                                                                   v_stride=4096)),
+                                               vp(P16), 0, vp(P16), None)
+    assert call(big, cu, T, 1) == 8  # GDN_ERR_SCRATCH
+    assert ops.status_string(8).startswith("the call needs more")
+    small = (ctypes.c_int32 * 3)(0, 100, 230)
+    bad = (ctypes.c_int32 * 3)(0, 150, 100)
+    assert call(d, bad, 230, 2) == SHAPE
+    assert call(dims(Hk=3), small, 230, 2) == SHAPE
+    assert call(dims(dk=96, dv=96), small, 230, 2) == UNSUPPORTED
+    zero = (ctypes.c_int32 * 3)(0, 0, 0)
+    assert call(d, zero, 0, 2) == OK  # nothing to do: no HIP call, nothing launched
