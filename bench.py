@@ -375,17 +375,41 @@ def deep_model_bench(torch, ops, synth, batches=(1, 32), layers=48, steps=(100, 
                 **res)
 
 
+PREFILL_OTHER_SHAPES = ((32, 32), (64, 64), (96, 96), (64, 128), (128, 64), (128, 256),
+                        (256, 128), (256, 256))
+
+
+def prefill_shapes_bench(torch, ops, synth, calls=10, warmup=2):
+    """The chunked prefill at the other built head shapes (the one-kernel f32 path):
+    one sequence of T=4096 and the 8-sequence varlen batch, Hk=16, Hv=32, bf16
+    N(0,1) inputs, raw gates, core output; tokens/s, and the state-and-activation
+    bytes per call over the call time against 8 TB/s."""
+    res = {}
+    for dk, dv in PREFILL_OTHER_SHAPES:
+        r = {}
+        for name, lengths, hm, std in (("T4096", (4096,), synth.GROUPED, 0.0),
+                                       ("varlen", VARLEN_LENGTHS, synth.TILED, 0.02)):
+            pre = prefill_bench(torch, ops, synth, lengths=lengths, head_map=hm, state_std=std,
+                                seed=3, calls=calls, warmup=warmup, dk=dk, dv=dv)
+            r[name] = dict(us_per_call=pre["ms_per_call"] * 1e3, tokens_per_s=pre["tokens_per_s"],
+                           hbm_frac=pre["roofline"]["frac"])
+        res[f"{dk}x{dv}"] = r
+    return dict(workload="chunked prefill per head shape (dk x dv), Hk=16, Hv=32, bf16 N(0,1), "
+                         "raw gates, f32 core output: one T=4096 sequence and the 8-sequence "
+                         "varlen batch (30,208 tokens)", **res)
+
+
 def prefill_bench(torch, ops, synth, *, lengths=(4096,), head_map=None, state_std=0.0,
-                  out_dtype=None, seed=3, calls=20, warmup=5, workload=None):
+                  out_dtype=None, seed=3, calls=20, warmup=5, workload=None, dk=128, dv=128):
     """Chunked prefill over packed sequences of the given lengths, Hk=16, Hv=32,
     d=128, bf16 N(0,1) inputs, raw gates with A_log ~ U[-2,0], q/k L2-normalised
     in-op, initial states N(0, state_std^2), core output (no gated norm). Defaults:
     config 3 (one sequence of 4096 tokens, grouped map, zero state, f32 out)."""
     dev = torch.device("cuda:0")
-    Hk, Hv, d = 16, 32, 128
+    Hk, Hv = 16, 32
     head_map = synth.GROUPED if head_map is None else head_map
     out_dtype = torch.float32 if out_dtype is None else out_dtype
-    P = synth.prefill(seed=seed, lengths=list(lengths), Hk=Hk, Hv=Hv, dk=d, dv=d,
+    P = synth.prefill(seed=seed, lengths=list(lengths), Hk=Hk, Hv=Hv, dk=dk, dv=dv,
                       head_map=head_map, state_std=state_std)
     T = int(P["cu_seqlens"][-1])
     N = len(lengths)
@@ -393,13 +417,13 @@ def prefill_bench(torch, ops, synth, *, lengths=(4096,), head_map=None, state_st
     q, k, v, a, b = g(P["q"]), g(P["k"]), g(P["v"]), g(P["a"]), g(P["b"])
     state0 = P["state"].to(dev).contiguous()
     state = state0.clone()
-    out = torch.empty((T, Hv, d), dtype=out_dtype, device=dev)
+    out = torch.empty((T, Hv, dv), dtype=out_dtype, device=dev)
     cu_h = P["cu_seqlens"].contiguous()
     cu_d = cu_h.to(dev)
-    need = ops.prefill_workspace_bytes(Hk=Hk, Hv=Hv, dk=d, dv=d, num_seqs=N, total_tokens=T)
+    need = ops.prefill_workspace_bytes(Hk=Hk, Hv=Hv, dk=dk, dv=dv, num_seqs=N, total_tokens=T)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    call = ops.prepare_prefill_chunked(q, k, v, state, cu_d, cu_h, out, ws, Hk=Hk, Hv=Hv, dk=d,
-                                       dv=d, head_map=head_map, a=a, b=b,
+    call = ops.prepare_prefill_chunked(q, k, v, state, cu_d, cu_h, out, ws, Hk=Hk, Hv=Hv, dk=dk,
+                                       dv=dv, head_map=head_map, a=a, b=b,
                                        decay_param=P["A_log"].to(dev),
                                        dt_bias=P["dt_bias"].to(dev))
     for _ in range(warmup):
@@ -421,10 +445,11 @@ def prefill_bench(torch, ops, synth, *, lengths=(4096,), head_map=None, state_st
     # algorithmic MFMA work of the chunked form, per (chunk, v-head): U, W (2 C^2 d
     # each), W S^T, Q S^T, D^T K (2 C d^2 each), Aqk D (2 C^2 d); per (chunk, k-head):
     # K K^T and Q K^T (2 C^2 d each)
-    flops = chunks * (Hv * (3 * 2 * C * C * d + 3 * 2 * C * d * d) + Hk * 2 * 2 * C * C * d)
+    flops = chunks * (Hv * (2 * C * C * dv + 2 * C * C * dk + 2 * C * C * dv + 3 * 2 * C * dk * dv)
+                      + Hk * 2 * 2 * C * C * dk)
     # HBM bytes: bf16 q, k, v, a, b in; the output; the states read and written once
     osz = 4 if out_dtype == torch.float32 else 2
-    hbm = T * (2 * Hk * d + Hv * d + 2 * Hv) * 2 + T * Hv * d * osz + 2 * N * Hv * d * d * 4
+    hbm = T * (2 * Hk * dk + Hv * dv + 2 * Hv) * 2 + T * Hv * dv * osz + 2 * N * Hv * dk * dv * 4
     t = ms * 1e-3
     return dict(workload=workload, tokens=T, sequences=N, chunks=chunks,
                 tokens_per_s=T / t, ms_per_call=ms, calls=calls, unit="tokens/s",
@@ -632,6 +657,8 @@ def main():
         print(f"[bench] varlen prefill {var['tokens_per_s'] / 1e6:.2f} M tokens/s, "
               f"{var['ms_per_call'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
         line["prefill_varlen"] = var
+        print("[bench] prefill per head shape", file=sys.stderr, flush=True)
+        line["prefill_head_shapes"] = prefill_shapes_bench(torch, ops, synth)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_conv.hip", "gdn_decode.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_conv.hip", "gdn_decode.hip", "gdn_prefill.hip",
+           "gdn_prefill_generic.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -101,9 +101,10 @@ __device__ __forceinline__ int vgpr_zero()
 // One element of runtime dtype `dt`, read without a branch: the 32-bit word
 // holding it is loaded (the base pointer is 4-byte aligned -- the host checks),
 // then the conversion is selected. Split into the load and the conversion so a
-// caller can issue other loads in between. Only for arrays with an even element
-// count (z: [tokens][Hv][dv] with dv even in every built shape), so the word of
-// a 16-bit element never reaches past the array's last element.
+// caller can issue other loads in between. Only for arrays read in runs of even
+// length from an even element (z: [tokens][Hv][dv] with dv even in every built
+// shape; q, k, v rows, 4-element aligned with even head dims), so the word of a
+// 16-bit element never reaches past the run's last element.
 __device__ __forceinline__ uint32_t load_word_nb(const void *p, int64_t idx, int dt)
 {
     const int64_t byte = dt == DT_F32 ? idx * 4 : idx * 2;

@@ -95,13 +95,18 @@ DecodePlan decode_plan(int dk, int dv, int B, int T, int Hv, bool fused_conv, ui
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
 // Which carry kernel a prefill runs: kind 0 = carry_split (compute and output waves
-// per slice), 1 = carry (one wave per slice); dv slices of 16 rows per workgroup;
+// per slice), 1 = carry (one wave per slice), 2 = the one-kernel f32 path of the
+// other head shapes (no prep kernel); dv slices of 16 rows per workgroup;
 // carry workgroups and threads per workgroup; prep workgroups. launch_prefill
 // launches exactly this for the device's compute-unit count.
 struct PrefillPlan {
     int carry_kind, slices_per_wg, carry_workgroups, carry_threads, prep_workgroups;
 };
 bool prefill_supported(int dk, int dv);
+// The one-kernel f32 path (gdn_prefill_generic.hip) for the shapes other than 128 x 128.
+bool prefill_generic_supported(int dk, int dv);
+int prefill_generic_chunk(int dk);
+hipError_t launch_prefill_generic(const PrefillParams &p, hipStream_t s);
 PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chunks, int cus);
 size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                int64_t total_tokens, bool norm);

@@ -1174,18 +1174,26 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillParams p)
 
 }  // namespace
 
-bool prefill_supported(int dk, int dv) { return dk == DH && dv == DH; }
+// 128 x 128 runs the MFMA kernels of this file; the decode's other head shapes
+// run the one-kernel f32 path of gdn_prefill_generic.hip.
+bool prefill_supported(int dk, int dv) { return (dk == DH && dv == DH) || prefill_generic_supported(dk, dv); }
+
+bool prefill_is_mfma(int dk, int dv) { return dk == DH && dv == DH; }
 
 size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                int64_t total_tokens, bool norm)
 {
-    (void)dk;
-    (void)dv;
+    if (!prefill_is_mfma(dk, dv))  // only the gated norm's f32 core output
+        return norm ? align256(sizeof(float) * (size_t)total_tokens * Hv * dv) : 256;
     return ws_layout(Hk, Hv, max_chunks, N, total_tokens, norm).total;
 }
 
 void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
 {
+    if (!prefill_is_mfma(p.hc.dk, p.hc.dv)) {
+        p.onorm = static_cast<float *>(ws);
+        return;
+    }
     const WsLayout L = ws_layout(p.hc.Hk, p.hc.Hv, max_chunks, p.N, p.total,
                                  (p.hc.flags & F_GATED_NORM) != 0);
     unsigned char *b = static_cast<unsigned char *>(ws);
@@ -1241,6 +1249,14 @@ PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chun
     PrefillPlan pl{};
     if (!prefill_supported(dk, dv))
         return pl;
+    if (!prefill_is_mfma(dk, dv)) {  // one workgroup per (sequence, v-head, 32 dv rows)
+        pl.carry_kind = 2;
+        pl.slices_per_wg = 2;
+        pl.carry_workgroups = (int)((int64_t)N * Hv * (dv / 32));
+        pl.carry_threads = 256;
+        pl.prep_workgroups = 0;
+        return pl;
+    }
     const int64_t groups = (int64_t)N * Hv;
     const int64_t rounded = (groups + 7) / 8 * 8;  // XCD-aware order: groups in blocks of 8
     if (groups * (DH / 16) <= cus) {
@@ -1265,6 +1281,8 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s)
 {
     if (p.num_chunks == 0)
         return hipSuccess;
+    if (!prefill_is_mfma(p.hc.dk, p.hc.dv))
+        return launch_prefill_generic(p, s);
     if (p.N > 1)  // one sequence: the chunk bounds are closed-form, no table
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p);
     int cus = 0;

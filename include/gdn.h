@@ -91,10 +91,9 @@ typedef struct gdn_dims {
     int32_t num_k_heads; /* Hk >= 1 */
     int32_t num_v_heads; /* Hv >= 1, Hv % Hk == 0 */
     int32_t head_dim_k;  /* dk */
-    int32_t head_dim_v;  /* dv. Built (dk, dv): decode step and layer (32,32), (64,64),
+    int32_t head_dim_v;  /* dv. Built (dk, dv), for every entry point: (32,32), (64,64),
                             (96,96), (128,128), (64,128), (128,64), (128,256),
-                            (256,128), (256,256);
-                            chunked prefill (128,128). Others: UNSUPPORTED. */
+                            (256,128), (256,256). Others: UNSUPPORTED. */
     int32_t head_map;    /* gdn_head_map */
     int32_t decay;       /* gdn_decay, used with GDN_RAW_GATES */
     uint32_t flags;      /* GDN_L2NORM_QK | GDN_RAW_GATES | GDN_GATED_NORM |
@@ -240,8 +239,10 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_seqs, int32
 
 /* ---------------------------------------------------------------------------
  * gdn_prefill_chunked -- the same recurrence over packed variable-length
- * sequences, computed chunk-parallel (64-token chunks that start at each
- * sequence's first token and never straddle two sequences). The result equals
+ * sequences, computed chunk-parallel (64-token chunks -- 32 when dk = 256 --
+ * that start at each sequence's first token and never straddle two
+ * sequences). dk = dv = 128 runs MFMA kernels with f16 operands; the other head
+ * shapes run one f32 kernel per (sequence, v-head, 32 dv rows). The result equals
  * the token-by-token recurrence up to rounding order (ferrox-core src/gdn.rs
  * module doc: the chunked form is the same recurrence summed in another order;
  * ferrum-kernels tests page, `chunked_c64_matches_recurrent_oracle_and_

@@ -161,7 +161,8 @@ def test_prefill_validation():
     assert call(ws_bytes=need - 1) == WORKSPACE
     assert call(ws=P16 + 16) == ALIGN
     assert call(d=dims(Hk=3)) == SHAPE
-    assert call(d=dims(dk=96, dv=96)) == UNSUPPORTED
+    assert call(d=dims(dk=96, dv=128)) == UNSUPPORTED       # not built
+    assert call(d=dims(dk=32, dv=64)) == UNSUPPORTED
     assert call(d=dims(flags=8)) == UNSUPPORTED            # GDN_STREAM_STATE: decode only
     # a gated-norm call with the plain workspace size is refused, not overrun
     assert call(d=dn, inp=inputs(z=vp(P16), norm_weight=vp(P16))) == WORKSPACE
@@ -309,6 +310,24 @@ def test_noalloc_prefill_rejects_what_its_scratch_cannot_hold():
     bad = (ctypes.c_int32 * 3)(0, 150, 100)
     assert call(d, bad, 230, 2) == SHAPE
     assert call(dims(Hk=3), small, 230, 2) == SHAPE
-    assert call(dims(dk=96, dv=96), small, 230, 2) == UNSUPPORTED
+    assert call(dims(dk=96, dv=128), small, 230, 2) == UNSUPPORTED
     zero = (ctypes.c_int32 * 3)(0, 0, 0)
     assert call(d, zero, 0, 2) == OK  # nothing to do: no HIP call, nothing launched
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 64), (96, 96), (64, 128), (128, 64), (128, 256),
+                                   (256, 128), (256, 256)])
+def test_prefill_other_head_shapes_take_the_one_kernel_path(dk, dv):
+    """Head shapes other than 128 x 128 run one f32 workgroup per (sequence, v-head,
+    32 dv rows) with no preparation kernel; 128 x 128 keeps the MFMA kernels."""
+    lengths = [100, 0, 37]
+    i = ops.prefill_launch_info(lengths, Hk=2, Hv=4, dk=dk, dv=dv, compute_units=256)
+    assert (i["carry_kind"], i["slices_per_workgroup"], i["prep_workgroups"]) == (2, 2, 0)
+    assert i["workgroups"] == len(lengths) * 4 * (dv // 32) and i["threads"] == 256
+    # its workspace is only the gated norm's f32 core output
+    d = dims(dk=dk, dv=dv)
+    assert ops.load().gdn_prefill_workspace_bytes(ctypes.byref(d), 3, 137) == 256
+    dn = dims(dk=dk, dv=dv, flags=ops.GATED_NORM)
+    assert ops.load().gdn_prefill_workspace_bytes(ctypes.byref(dn), 3, 137) >= 137 * 4 * dv * 4
+    i = ops.prefill_launch_info(lengths, Hk=2, Hv=4, dk=128, dv=128, compute_units=256)
+    assert i["carry_kind"] in (0, 1) and i["prep_workgroups"] > 0

@@ -413,3 +413,97 @@ def test_prefill_bad_offsets_leave_state_untouched():
     assert e.value.status == 2
     torch.cuda.synchronize()
     assert torch.equal(st, before)
+
+
+# ------------------------------------------------------------------ other head shapes (one-kernel f32 path)
+
+OTHER_SHAPES = [(32, 32), (64, 64), (96, 96), (64, 128), (128, 64), (128, 256), (256, 128),
+                (256, 256)]
+
+
+@pytest.mark.parametrize("Hk,Hv", [(2, 4), (2, 2)])
+@pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
+def test_page_chunk_core_d32_145_tokens_split_73_with_sentinel(Hk, Hv, head_map):
+    """The ferrum-kernels page's own chunked-core shape, (Hk, Hv, dk, dv) = (2, 4, 32,
+    32) (and (2, 2, 32, 32)), on that test's sin-pattern inputs: T = 145 against the
+    token-by-token oracle, and split at token 73 (not chunk-aligned) across two
+    calls, with sentinels around the state
+    (`chunked_c64_matches_recurrent_oracle_and_non_aligned_state_continuity`)."""
+    P = core_workload(145, Hk, Hv, 32, head_map)
+    out, out_split, st, st_split = split_with_sentinel(P, 73, raw=False)
+    y, S = oracle_seq(P, 0, f64(P["state"][0]), raw=False)
+    assert np.any(np.abs(f64(out)) > 1e-4)
+    assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(out_split), y) <= TOL_OUT
+    assert maxabs(f64(st[0]), S) <= TOL_STATE and maxabs(f64(st_split[0]), S) <= TOL_STATE
+    assert maxabs(f64(st_split), f64(st)) <= TOL_STATE
+
+
+@pytest.mark.parametrize("dk,dv", OTHER_SHAPES)
+@pytest.mark.parametrize("head_map", [synth.GROUPED, synth.TILED])
+def test_other_head_shapes_ragged_varlen(dk, dv, head_map):
+    """Ragged packed sequences (an empty one, a single token, lengths around the 32-
+    and 64-token chunk edges) with nonzero initial states, raw gates and bf16 N(0,1)
+    inputs, every head and state compared with the oracle."""
+    lengths = [0, 1, 31, 33, 64, 65, 150]
+    P = synth.prefill(seed=60 + dk + dv, lengths=lengths, Hk=2, Hv=4, dk=dk, dv=dv,
+                      head_map=head_map, state_std=0.05)
+    out, st = run_prefill(P)
+    torch.cuda.synchronize()
+    y, S = oracle.packed(f64(P["q"]), f64(P["k"]), f64(P["v"]), f64(P["state"]), head_map,
+                         P["cu_seqlens"], a=f64(P["a"]), b=f64(P["b"]),
+                         decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]),
+                         nthreads=threads())
+    assert torch.equal(st[0].cpu(), P["state"][0]), "empty sequence changed its state"
+    assert maxabs(f64(out), y) <= TOL_OUT
+    assert maxabs(f64(st), S) <= TOL_STATE
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (96, 96), (256, 128)])
+@pytest.mark.parametrize("act", [torch.float32, torch.float16])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_other_head_shapes_dtypes_and_gated_norm(dk, dv, act, out_dtype):
+    lengths = [100, 37]
+    P = synth.prefill(seed=70 + dk, lengths=lengths, Hk=2, Hv=4, dk=dk, dv=dv,
+                      head_map=synth.GROUPED, dtype=act, state_std=0.02, with_z=True)
+    out, st = run_prefill(P, out_dtype=out_dtype, gated=True)
+    torch.cuda.synchronize()
+    y, S = oracle.packed(f64(P["q"]), f64(P["k"]), f64(P["v"]), f64(P["state"]), synth.GROUPED,
+                         P["cu_seqlens"], a=f64(P["a"]), b=f64(P["b"]),
+                         decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]), z=f64(P["z"]),
+                         norm_w=f64(P["norm_w"]), nthreads=threads())
+    bound = TOL_OUT if out_dtype == torch.float32 else ulp16(y, out_dtype) + TOL_OUT
+    assert np.all(np.abs(f64(out) - y) <= bound)
+    assert maxabs(f64(st), S) <= TOL_STATE
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 256)])
+def test_other_head_shapes_negative_rate_and_unnormalised(dk, dv):
+    """NegativeRate decay with the in-op L2 norm, then un-normalised LCG inputs with
+    given gates and weak decay (the regime where the carried state matters most)."""
+    P = synth.prefill(seed=75, lengths=[145], Hk=2, Hv=4, dk=dk, dv=dv, head_map=synth.TILED,
+                      state_std=0.05)
+    P["A_log"] = synth.negative_rates(75, 4)
+    dec = ops.DECAY_NEGATIVE_RATE
+    out, out_split, st, st_split = split_with_sentinel(P, 73, decay=dec)
+    y, S = oracle_seq(P, 0, f64(P["state"][0]), decay=dec)
+    assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(out_split), y) <= TOL_OUT
+    assert maxabs(f64(st[0]), S) <= TOL_STATE and maxabs(f64(st_split[0]), S) <= TOL_STATE
+    L = synth.lcg_prefill(T=145, Hk=2, Hv=4, dk=dk, dv=dv, qk_scale=0.15 * (128 / dk) ** 0.5)
+    L["head_map"] = synth.GROUPED
+    out, out_split, st, st_split = split_with_sentinel(L, 73, raw=False, l2norm_qk=False)
+    y, S = oracle_seq(L, 0, f64(L["state"][0]), raw=False, l2norm_qk=False)
+    assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(out_split), y) <= TOL_OUT
+    assert maxabs(f64(st[0]), S) <= TOL_STATE and maxabs(f64(st_split[0]), S) <= TOL_STATE
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
+def test_other_head_shapes_long_sequence(dk, dv):
+    """T = 2048 (32 chunks) at the config-3 statistics (bf16 N(0,1), zero state)."""
+    P = synth.prefill(seed=77, lengths=[2048], Hk=4, Hv=8, dk=dk, dv=dv, head_map=synth.GROUPED)
+    out, st = run_prefill(P)
+    torch.cuda.synchronize()
+    y, S = oracle.packed(f64(P["q"]), f64(P["k"]), f64(P["v"]), f64(P["state"]), synth.GROUPED,
+                         P["cu_seqlens"], a=f64(P["a"]), b=f64(P["b"]),
+                         decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]),
+                         nthreads=threads())
+    assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(st), S) <= TOL_STATE
