@@ -60,20 +60,20 @@ def kernel_source_hash(names):
     return h.hexdigest()[:16]
 
 
-def read_traffic(summary_name, source_hash):
+def read_traffic(summary_name, source_hash, key="hbm_bytes_per_dispatch"):
     """Bytes per dispatch from a committed counter summary, if it matches the source."""
     path = os.path.join(ROOT, "profiles", summary_name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", text)
+    t = re.search(key + r":\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != source_hash:
         return None
     return float(t.group(1))
 
 
-def decode_bench(args, torch, ops, synth):
+def decode_bench(args, torch, ops, synth, rot_steps=ROTATING_STEPS):
     """The headline: B=64 decode steps, each one gdn_decode_layer launch (conv +
     L2 norm + gates + recurrence + gated norm), with the conv state alternating
     between two buffers; then the same step as gdn_conv_update + gdn_decode_step
@@ -164,7 +164,7 @@ def decode_bench(args, torch, ops, synth):
     for _ in range(nsets * 4):
         for S in sets:
             step(S, "layer_stream")
-    Kr = ROTATING_STEPS
+    Kr = rot_steps
     ms_rot, _ = timed(lambda i: step(sets[i % nsets], "layer_stream"), Kr)
     for _ in range(nsets * 4):
         for S in sets:
@@ -193,6 +193,8 @@ def decode_bench(args, torch, ops, synth):
                                  unit="GB/s", frac=rot_achieved / HBM_PEAK_GBS,
                                  kernel="gdn decode_kernel<dk=128,dv=128,waves=16,bf16,conv K=4,"
                                         "non-temporal> (gdn_decode_layer, GDN_STREAM_STATE)",
+                                 traffic=read_traffic("decode_layer_b64_bf16_traffic.md", src_hash,
+                                                      "stream_bytes_per_dispatch"),
                                  bytes_per_launch=dec_bytes, avg_launch_us=ms_rot * 1e3,
                                  steps=Kr, state="streamed: 4 state sets, 537 MB, cycled"),
         two_launch=dict(step="gdn_conv_update + gdn_decode_step", ms_per_step=ms_two,
@@ -451,11 +453,18 @@ def prefill_bench(torch, ops, synth, *, lengths=(4096,), head_map=None, state_st
     osz = 4 if out_dtype == torch.float32 else 2
     hbm = T * (2 * Hk * dk + Hv * dv + 2 * Hv) * 2 + T * Hv * dv * osz + 2 * N * Hv * dk * dv * 4
     t = ms * 1e-3
+    traffic = None
+    if tuple(lengths) == (4096,) and (dk, dv) == (128, 128):
+        traffic = read_traffic("prefill_t4096_traffic.md",
+                               kernel_source_hash(["gdn_prefill.hip", "gdn_device.h", "gdn_kernels.h"]))
     return dict(workload=workload, tokens=T, sequences=N, chunks=chunks,
                 tokens_per_s=T / t, ms_per_call=ms, calls=calls, unit="tokens/s",
                 mfma_flops=flops, mfma_util=flops / t / (MFMA_F16_PEAK_TFLOPS * 1e12),
                 roofline=dict(bound="hbm", achieved=hbm / t / 1e9, peak=HBM_PEAK_GBS,
-                              unit="GB/s", frac=hbm / t / 1e9 / HBM_PEAK_GBS, bytes=hbm))
+                              unit="GB/s", frac=hbm / t / 1e9 / HBM_PEAK_GBS, bytes=hbm,
+                              traffic=traffic, traffic_note="L2-to-fabric bytes per call (prep + "
+                              "carry), from the committed counter summary when it matches the "
+                              "sources; the excess over `bytes` is the workspace's round trip"))
 
 
 def counter_pass(torch, ops, synth, steps=10, copy_mib=256):
@@ -465,7 +474,7 @@ def counter_pass(torch, ops, synth, steps=10, copy_mib=256):
     (read and written once each: 2 * copy_mib MiB of traffic per dispatch), whose
     counter readings calibrate the decode kernels'."""
     args = argparse.Namespace(warmup=2, steps=steps)
-    decode_bench(args, torch, ops, synth)
+    decode_bench(args, torch, ops, synth, rot_steps=4 * steps)
     prefill_bench(torch, ops, synth, calls=3, warmup=1)
     n = copy_mib * 2 ** 20 // 4
     src = torch.randn(n, device="cuda:0")
