@@ -14,9 +14,9 @@
 //
 // Design: one workgroup of 256 threads per (sequence, v-head, 32-row slice of
 // dv), sequential over the sequence's chunks, with the slice's f32 state resident
-// in LDS for the whole call. Every product is f32 on the vector ALUs, each
-// thread owning a small register tile of the result and reading its operands
-// from LDS rows padded to an odd length. No workspace except the f32 core
+// in LDS for the whole call. Every product runs on f32 MFMA (16 x 16 x 4), its
+// operands read from LDS rows padded to an odd length; the next chunk's inputs
+// are loaded into registers while the current one is computed. No workspace except the f32 core
 // output the gated norm reads. Chunks are 64 tokens, 32 when dk = 256 (the LDS
 // holds the chunk's K and Q/W rows and the state slice: 125-159 KB).
 
@@ -35,44 +35,38 @@ constexpr int gen_chunk()
     return DK >= 256 ? 32 : 64;
 }
 
-// C[m][n] (m < M, n < N) for 256 threads, thread (ty, tx) owning rows
-// ty*RM .. +RM-1 and columns tx*RN .. +RN-1 with RM = M/16, RN = N/16:
-// acc[r][c] = sum_k a(m, k) b(k, n), then c(m, n, acc).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// C[m][n] = sum_k a(m, k) b(k, n) for m < M, n < N on v_mfma_f32_16x16x4_f32 (f32
+// operands, f32 accumulation). The 16 x 16 output tiles are dealt to the 4 waves,
+// two at a time so that consecutive products go to different accumulators; lane
+// (li, lg) = (lane % 16, lane / 16) feeds a(m0 + li, k0 + lg) and b(k0 + lg,
+// n0 + li) and receives C[m0 + 4 lg + r][n0 + li] in acc[r], handed to
+// c(m, n, value).
 template <int M, int N, int K, class FA, class FB, class FC>
-__device__ __forceinline__ void tile_product(FA a, FB b, FC c)
+__device__ __forceinline__ void mfma_product(FA a, FB b, FC c)
 {
-    constexpr int RM = M / 16, RN = N / 16;
-    static_assert(M % 16 == 0 && N % 16 == 0, "16 x 16 thread grid");
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    // loads of several k steps in flight at once, within ~64 operand registers
-    constexpr int U = (RM + RN) >= 16 ? 2 : (RM + RN) >= 8 ? 4 : 8;
-    static_assert(K % U == 0, "unrolled k loop");
-    float acc[RM][RN];
+    constexpr int TN = N / 16, NT = (M / 16) * TN;
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "16 x 16 x 4 tiles");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    for (int t = wave; t < NT; t += 8) {
+        const int t2 = t + 4 < NT ? t + 4 : t;  // a second tile, or the first again
+        const int m0 = (t / TN) * 16, n0 = (t % TN) * 16, m1 = (t2 / TN) * 16, n1 = (t2 % TN) * 16;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k0 = 0; k0 < K; k0 += 4) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m0 + li, k0 + lg), b(k0 + lg, n0 + li), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m1 + li, k0 + lg), b(k0 + lg, n1 + li), acc1, 0, 0, 0);
+        }
 #pragma unroll
-    for (int r = 0; r < RM; ++r)
+        for (int r = 0; r < 4; ++r)
+            c(m0 + 4 * lg + r, n0 + li, acc0[r]);
+        if (t2 != t) {
 #pragma unroll
-        for (int q = 0; q < RN; ++q)
-            acc[r][q] = 0.f;
-#pragma unroll U
-    for (int k = 0; k < K; ++k) {
-        float av[RM], bv[RN];
-#pragma unroll
-        for (int r = 0; r < RM; ++r)
-            av[r] = a(ty * RM + r, k);
-#pragma unroll
-        for (int q = 0; q < RN; ++q)
-            bv[q] = b(k, tx * RN + q);
-#pragma unroll
-        for (int r = 0; r < RM; ++r)
-#pragma unroll
-            for (int q = 0; q < RN; ++q)
-                acc[r][q] = fmaf(av[r], bv[q], acc[r][q]);
+            for (int r = 0; r < 4; ++r)
+                c(m1 + 4 * lg + r, n1 + li, acc1[r]);
+        }
     }
-#pragma unroll
-    for (int r = 0; r < RM; ++r)
-#pragma unroll
-        for (int q = 0; q < RN; ++q)
-            c(ty * RM + r, tx * RN + q, acc[r][q]);
 }
 
 template <int DK, int DV>
@@ -113,22 +107,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
     for (int e = tid; e < kSlice * DK; e += kThreads)
         Ss[e / DK][e % DK] = Sg[e];
 
-    for (int c0 = 0; c0 < len; c0 += CC) {
+    // -- a chunk's inputs as raw words, every load issued before any is used and
+    // no branch around a load: addresses are clamped into the chunk (rows past its
+    // end re-read row n-1, columns past dk re-read column dk-1) and the values
+    // masked where they are used; each element comes as the 32-bit word holding it
+    // (a q/k/v row has an even length from a 4-element aligned start, so the word
+    // stays in the row) and the dtype is a select. Wave w takes rows w, w + 4, ...;
+    // lane l holds columns l, l + 64, ...; wave 0's lane t holds token t's gates.
+    // The next chunk's words are requested as soon as the current ones are in LDS,
+    // so their round trip overlaps the current chunk's products.
+    constexpr int RW = CC / 4, EPL = (DK + 63) / 64, VPT = CC * kSlice / kThreads;
+    const int qdt = in.qkv_dt;
+    uint32_t kw[RW][EPL], qw[RW][EPL], vw[VPT];
+    const void *gsa = raw ? in.a : static_cast<const void *>(in.g);
+    const void *gsb = raw ? in.b : static_cast<const void *>(in.beta);
+    const int gdt = raw ? in.ab_dt : DT_F32;
+    GateWord ga, gb;
+    const float dparam = raw ? in.decay_param[h] : 0.f, dtb = raw ? in.dt_bias[h] : 0.f;
+    auto issue = [&](int c0) {
         const int n = min(CC, len - c0);
         const int64_t tok0 = start + c0;
-        __syncthreads();  // the previous chunk is done with every buffer
-
-        // -- keys, queries and the slice's v rows: every load of the chunk is
-        // issued before any is used (one memory round trip per chunk), without a
-        // branch around any of them: addresses are clamped into the chunk (rows past
-        // its end re-read row n-1, columns past dk re-read column dk-1) and the
-        // values masked after; each element comes as the 32-bit word holding it (a
-        // q/k/v row has an even length from a 4-element aligned start, so the word
-        // stays in the row) and the dtype is a select. Wave w takes rows w, w + 4,
-        // ...; lane l holds columns l, l + 64, ...
-        constexpr int RW = CC / 4, EPL = (DK + 63) / 64, VPT = CC * kSlice / kThreads;
-        const int qdt = in.qkv_dt;
-        uint32_t kw[RW][EPL], qw[RW][EPL], vw[VPT];
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             const int64_t row = tok0 + min(wave + 4 * i, n - 1);
@@ -145,13 +143,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
             const int64_t row = tok0 + min(e / kSlice, n - 1);
             vw[i] = load_word_nb(in.v, row * in.v_stride + (int64_t)h * DV + dv0 + e % kSlice, qdt);
         }
-        // the gate inputs of token lane (wave 0), also before any use
-        const void *gsa = raw ? in.a : static_cast<const void *>(in.g);
-        const void *gsb = raw ? in.b : static_cast<const void *>(in.beta);
-        const int gdt = raw ? in.ab_dt : DT_F32;
         const int64_t gi = (tok0 + min(lane, n - 1)) * Hv + h;
-        const GateWord ga = load_gate(gsa, gi, gdt), gb = load_gate(gsb, gi, gdt);
-        const float dparam = raw ? in.decay_param[h] : 0.f, dtb = raw ? in.dt_bias[h] : 0.f;
+        ga = load_gate(gsa, gi, gdt);
+        gb = load_gate(gsb, gi, gdt);
+    };
+    issue(0);
+
+    for (int c0 = 0; c0 < len; c0 += CC) {
+        const int n = min(CC, len - c0);
+        const int64_t tok0 = start + c0;
+        __syncthreads();  // the previous chunk is done with every buffer
+
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             const int r = wave + 4 * i;
@@ -188,8 +190,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
         }
         // -- gates and their in-chunk prefix sums (wave 0, lane = token); tokens
         // past the chunk's end get g = beta = 0, so they carry G_{n-1}
+        float g = gate_value(ga, gdt), beta = gate_value(gb, gdt);
+        if (c0 + CC < len)
+            issue(c0 + CC);  // the next chunk's words, in flight from here
         if (wave == 0) {
-            float g = gate_value(ga, gdt), beta = gate_value(gb, gdt);
             if (raw) {
                 const float rate = hc.decay_kind == 0 ? -expf(dparam) : dparam;
                 g = rate * softplus_f(g + dtb);
@@ -216,13 +220,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
         __syncthreads();
 
         // -- A, Aqk and Q S^T (the entering state)
-        tile_product<CC, CC, DK>([&](int t, int i) { return Kc[t][i]; }, [&](int i, int s) { return Kc[s][i]; },
+        mfma_product<CC, CC, DK>([&](int t, int i) { return Kc[t][i]; }, [&](int i, int s) { return Kc[s][i]; },
                                  [&](int t, int s, float v) {
                                      Am[t][s] = s < t ? beta_s[t] * expf(G_s[t] - G_s[s]) * v : 0.f;
                                  });
-        tile_product<CC, CC, DK>([&](int t, int i) { return Qc[t][i]; }, [&](int i, int s) { return Kc[s][i]; },
+        mfma_product<CC, CC, DK>([&](int t, int i) { return Qc[t][i]; }, [&](int i, int s) { return Kc[s][i]; },
                                  [&](int t, int s, float v) { Aq[t][s] = s <= t ? expf(G_s[t] - G_s[s]) * v : 0.f; });
-        tile_product<CC, kSlice, DK>([&](int t, int i) { return Qc[t][i]; },
+        mfma_product<CC, kSlice, DK>([&](int t, int i) { return Qc[t][i]; },
                                      [&](int i, int j) { return Ss[j][i]; },
                                      [&](int t, int j, float v) { Qs[t][j] = v; });
         __syncthreads();
@@ -258,8 +262,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
             for (int e = tid; e < (NB - L) * 256; e += kThreads) {
                 const int j = e >> 8, i = j + L, r = (e >> 4) & 15, c = e & 15;
                 float acc = 0.f;
-                for (int s2 = 16 * j; s2 < 16 * i; ++s2)
-                    acc = fmaf(Am[16 * i + r][s2], Tm[s2][16 * j + c], acc);
+                for (int kb = j; kb < i; ++kb) {
+                    float part = 0.f;  // one 16-long block: loads issued together
+#pragma unroll
+                    for (int s2 = 0; s2 < 16; ++s2)
+                        part = fmaf(Am[16 * i + r][16 * kb + s2], Tm[16 * kb + s2][16 * j + c], part);
+                    acc += part;
+                }
                 Mb[j][r][c] = acc;
             }
             __syncthreads();
@@ -275,16 +284,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
         }
 
         // -- W = T diag(beta gamma) K (into Qc) and U = T diag(beta) V
-        tile_product<CC, DK, CC>([&](int t, int s) { return Tm[t][s] * bg_s[s]; },
+        mfma_product<CC, DK, CC>([&](int t, int s) { return Tm[t][s] * bg_s[s]; },
                                  [&](int s, int i) { return Kc[s][i]; },
                                  [&](int t, int i, float v) { Qc[t][i] = v; });
-        tile_product<CC, kSlice, CC>([&](int t, int s) { return Tm[t][s] * beta_s[s]; },
+        mfma_product<CC, kSlice, CC>([&](int t, int s) { return Tm[t][s] * beta_s[s]; },
                                      [&](int s, int j) { return Vs[s][j]; },
                                      [&](int t, int j, float v) { Us[t][j] = v; });
         __syncthreads();
 
         // -- D = U - W S^T (in place)
-        tile_product<CC, kSlice, DK>([&](int t, int i) { return Qc[t][i]; },
+        mfma_product<CC, kSlice, DK>([&](int t, int i) { return Qc[t][i]; },
                                      [&](int i, int j) { return Ss[j][i]; },
                                      [&](int t, int j, float v) { Us[t][j] -= v; });
         __syncthreads();
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
         {
             void *obase = (flags & F_GATED_NORM) ? static_cast<void *>(p.onorm) : p.out;
             const int odt = (flags & F_GATED_NORM) ? DT_F32 : p.out_dt;
-            tile_product<CC, kSlice, CC>([&](int t, int s) { return Aq[t][s]; },
+            mfma_product<CC, kSlice, CC>([&](int t, int s) { return Aq[t][s]; },
                                          [&](int s, int j) { return Us[s][j]; },
                                          [&](int t, int j, float v) {
                                              if (t < n)
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_generic_kernel(PrefillPar
                                                            hc.scale * fmaf(gam_s[t], Qs[t][j], v));
                                          });
             const float gl = gam_s[CC - 1];
-            tile_product<kSlice, DK, CC>([&](int j, int t) { return Us[t][j] * ev_s[t]; },
+            mfma_product<kSlice, DK, CC>([&](int j, int t) { return Us[t][j] * ev_s[t]; },
                                          [&](int t, int i) { return Kc[t][i]; },
                                          [&](int j, int i, float v) { Ss[j][i] = fmaf(gl, Ss[j][i], v); });
         }
