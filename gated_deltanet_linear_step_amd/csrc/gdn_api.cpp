@@ -123,8 +123,10 @@ gdn_status check_common(const gdn_dims *d, const gdn_inputs *in, int32_t out_dty
 
 gdn_status launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
 
-// Validates host cu_seqlens; fills the chunk counts the prefill grid needs.
-gdn_status check_cu(const int32_t *cu, int32_t n, int32_t total, int64_t *chunks, int64_t *max_chunks)
+// Validates host cu_seqlens; fills the chunk counts (chunks of `clen` tokens) the
+// prefill grid needs.
+gdn_status check_cu(const int32_t *cu, int32_t n, int32_t total, int clen, int64_t *chunks,
+                    int64_t *max_chunks)
 {
     if (cu[0] != 0 || cu[n] != total)
         return GDN_ERR_SHAPE;
@@ -132,7 +134,7 @@ gdn_status check_cu(const int32_t *cu, int32_t n, int32_t total, int64_t *chunks
     for (int32_t i = 0; i < n; ++i) {
         if (cu[i + 1] < cu[i])
             return GDN_ERR_SHAPE;
-        const int64_t ci = ((int64_t)cu[i + 1] - cu[i] + gdn::kChunk - 1) / gdn::kChunk;
+        const int64_t ci = ((int64_t)cu[i + 1] - cu[i] + clen - 1) / clen;
         c += ci;
         if (ci > mx)
             mx = ci;
@@ -140,6 +142,13 @@ gdn_status check_cu(const int32_t *cu, int32_t n, int32_t total, int64_t *chunks
     *chunks = c;
     *max_chunks = mx;
     return GDN_OK;
+}
+
+// An upper bound on a call's chunk count over every split of total_tokens into
+// num_seqs sequences: total / chunk length + one partial chunk per sequence.
+int64_t max_chunk_bound(const gdn_dims *d, int32_t num_seqs, int32_t total_tokens)
+{
+    return (int64_t)total_tokens / gdn::prefill_chunk_len(d->head_dim_k, d->head_dim_v) + num_seqs;
 }
 
 // Everything gdn_prefill_chunked checks except the workspace; fills the kernel
@@ -161,12 +170,13 @@ gdn_status prefill_prepare(const gdn_dims *dims, int32_t num_seqs, const int32_t
     if (num_seqs == 0)
         return total_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
     int64_t chunks = 0, max_chunks = 0;
-    st = check_cu(cu_seqlens_host, num_seqs, total_tokens, &chunks, &max_chunks);
+    const int clen = gdn::prefill_chunk_len(dims->head_dim_k, dims->head_dim_v);
+    st = check_cu(cu_seqlens_host, num_seqs, total_tokens, clen, &chunks, &max_chunks);
     if (st != GDN_OK)
         return st;
     if ((int64_t)total_tokens * dims->num_v_heads > kI32Max || chunks * dims->num_v_heads > kI32Max)
         return GDN_ERR_OVERFLOW;
-    const int64_t mc = (int64_t)total_tokens / gdn::kChunk + num_seqs;
+    const int64_t mc = (int64_t)total_tokens / clen + num_seqs;
     need = gdn::prefill_workspace_bytes(dims->num_k_heads, dims->num_v_heads, dims->head_dim_k,
                                         dims->head_dim_v, mc, num_seqs, total_tokens,
                                         (dims->flags & GDN_GATED_NORM) != 0);
@@ -269,7 +279,9 @@ gdn_status gdn_prefill_launch_info(const gdn_dims *d, int32_t num_seqs, const in
     if ((d->flags & ~kPrefillFlags) != 0 || !gdn::prefill_supported(d->head_dim_k, d->head_dim_v))
         return GDN_ERR_UNSUPPORTED;
     int64_t chunks = 0, max_chunks = 0;
-    const gdn_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens, &chunks, &max_chunks);
+    const gdn_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens,
+                                   gdn::prefill_chunk_len(d->head_dim_k, d->head_dim_v), &chunks,
+                                   &max_chunks);
     if (st != GDN_OK)
         return st;
     const gdn::PrefillPlan pl = gdn::prefill_plan(num_seqs, d->num_k_heads, d->num_v_heads,
@@ -406,7 +418,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims *d, int32_t num_seqs, int32_t 
     if (!d || num_seqs < 0 || total_tokens < 0 || d->num_k_heads < 1 || d->num_v_heads < 1 ||
         d->num_v_heads % d->num_k_heads != 0 || !gdn::prefill_supported(d->head_dim_k, d->head_dim_v))
         return 0;
-    const int64_t max_chunks = (int64_t)total_tokens / gdn::kChunk + num_seqs;
+    const int64_t max_chunks = max_chunk_bound(d, num_seqs, total_tokens);
     return gdn::prefill_workspace_bytes(d->num_k_heads, d->num_v_heads, d->head_dim_k,
                                         d->head_dim_v, max_chunks, num_seqs, total_tokens,
                                         (d->flags & GDN_GATED_NORM) != 0);
@@ -431,7 +443,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims *dims, int32_t num_seqs,
         return GDN_ERR_ALIGN;
     if (empty)
         return GDN_OK;  // every sequence empty: states untouched
-    gdn::prefill_carve(p, workspace, (int64_t)total_tokens / gdn::kChunk + num_seqs);
+    gdn::prefill_carve(p, workspace, max_chunk_bound(dims, num_seqs, total_tokens));
     return launch_status(gdn::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -452,7 +464,7 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_dims *dims, int32_t num_seqs,
     void *ws = nullptr;
     if (scratch_address(&ws) != hipSuccess)
         return GDN_ERR_LAUNCH;
-    gdn::prefill_carve(p, ws, (int64_t)total_tokens / gdn::kChunk + num_seqs);
+    gdn::prefill_carve(p, ws, max_chunk_bound(dims, num_seqs, total_tokens));
     return launch_status(gdn::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -67,7 +67,7 @@ struct PrefillParams {
     int out_dt;
     int N, total;
     const int32_t *cu;  // device [N+1]
-    int num_chunks;     // sum over sequences of ceil(len / 64)
+    int num_chunks;     // sum over sequences of ceil(len / chunk length)
     int max_seq_chunks; // largest per-sequence chunk count
     // workspace carve-out (device pointers)
     int32_t *chunk_seq;    // [num_chunks] sequence of each chunk
@@ -82,6 +82,12 @@ struct PrefillParams {
     uint16_t *aqk;         // [num_chunks][Hv][64][64]   f16, -scale (masked decayed Q K^T)
     float *gcum;           // [num_chunks][Hv][4][64]    f32, exp(G_t), -exp(G_last - G_t), scale exp(G_t), 0
     float *onorm;          // [total][Hv][dv]            f32 core output (gated norm only)
+    // the f32 path of the other head shapes (C = its chunk length), all f32
+    float *gq, *gk;        // [num_chunks][Hk][C][dk]    normalised q, k rows
+    float *gw;             // [num_chunks][Hv][C][dk]    W = T diag(beta gamma) K
+    float *gu;             // [num_chunks][Hv][C][dv]    U = T diag(beta) V
+    float *gaq;            // [num_chunks][Hv][C][C]     scale * (masked decayed Q K^T)
+    float *gdec;           // [num_chunks][Hv][3][C]     scale gamma_t, exp(G_last - G_t), gamma_t
 };
 
 // Which decode kernel a call runs: waves per workgroup, lanes per state row, token
@@ -106,7 +112,12 @@ bool prefill_supported(int dk, int dv);
 // The one-kernel f32 path (gdn_prefill_generic.hip) for the shapes other than 128 x 128.
 bool prefill_generic_supported(int dk, int dv);
 int prefill_generic_chunk(int dk);
+size_t prefill_generic_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
+                                       int64_t total_tokens, bool norm);
+void prefill_generic_carve(PrefillParams &p, void *ws, int64_t max_chunks);
 hipError_t launch_prefill_generic(const PrefillParams &p, hipStream_t s);
+// Tokens per chunk of the prefill that serves (dk, dv): 64, or 32 for the f32 path at dk = 256.
+int prefill_chunk_len(int dk, int dv);
 PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chunks, int cus);
 size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                int64_t total_tokens, bool norm);

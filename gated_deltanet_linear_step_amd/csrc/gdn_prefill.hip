@@ -1180,18 +1180,21 @@ bool prefill_supported(int dk, int dv) { return (dk == DH && dv == DH) || prefil
 
 bool prefill_is_mfma(int dk, int dv) { return dk == DH && dv == DH; }
 
+int prefill_chunk_len(int dk, int dv) { return prefill_is_mfma(dk, dv) ? C : prefill_generic_chunk(dk); }
+
+// max_chunks bounds the chunk count of the call (total / chunk length + N).
 size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                int64_t total_tokens, bool norm)
 {
-    if (!prefill_is_mfma(dk, dv))  // only the gated norm's f32 core output
-        return norm ? align256(sizeof(float) * (size_t)total_tokens * Hv * dv) : 256;
+    if (!prefill_is_mfma(dk, dv))
+        return prefill_generic_workspace_bytes(Hk, Hv, dk, dv, max_chunks, N, total_tokens, norm);
     return ws_layout(Hk, Hv, max_chunks, N, total_tokens, norm).total;
 }
 
 void prefill_carve(PrefillParams &p, void *ws, int64_t max_chunks)
 {
     if (!prefill_is_mfma(p.hc.dk, p.hc.dv)) {
-        p.onorm = static_cast<float *>(ws);
+        prefill_generic_carve(p, ws, max_chunks);
         return;
     }
     const WsLayout L = ws_layout(p.hc.Hk, p.hc.Hv, max_chunks, p.N, p.total,
@@ -1249,12 +1252,12 @@ PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chun
     PrefillPlan pl{};
     if (!prefill_supported(dk, dv))
         return pl;
-    if (!prefill_is_mfma(dk, dv)) {  // one workgroup per (sequence, v-head, 32 dv rows)
+    if (!prefill_is_mfma(dk, dv)) {  // f32 path: carry per (sequence, v-head, 32 dv rows)
         pl.carry_kind = 2;
         pl.slices_per_wg = 2;
         pl.carry_workgroups = (int)((int64_t)N * Hv * (dv / 32));
         pl.carry_threads = 256;
-        pl.prep_workgroups = 0;
+        pl.prep_workgroups = (int)(num_chunks * Hk);
         return pl;
     }
     const int64_t groups = (int64_t)N * Hv;

@@ -318,16 +318,24 @@ def test_noalloc_prefill_rejects_what_its_scratch_cannot_hold():
 @pytest.mark.parametrize("dk,dv", [(32, 32), (64, 64), (96, 96), (64, 128), (128, 64), (128, 256),
                                    (256, 128), (256, 256)])
 def test_prefill_other_head_shapes_take_the_one_kernel_path(dk, dv):
-    """Head shapes other than 128 x 128 run one f32 workgroup per (sequence, v-head,
-    32 dv rows) with no preparation kernel; 128 x 128 keeps the MFMA kernels."""
+    """Head shapes other than 128 x 128 run the f32 path: a preparation kernel per
+    (chunk, k-head) and a carry per (sequence, v-head, 32 dv rows), with 64-token
+    chunks (32 at dk = 256); 128 x 128 keeps the f16-operand MFMA kernels."""
     lengths = [100, 0, 37]
+    clen = 32 if dk == 256 else 64
+    chunks = sum((n + clen - 1) // clen for n in lengths)
     i = ops.prefill_launch_info(lengths, Hk=2, Hv=4, dk=dk, dv=dv, compute_units=256)
-    assert (i["carry_kind"], i["slices_per_workgroup"], i["prep_workgroups"]) == (2, 2, 0)
+    assert (i["carry_kind"], i["slices_per_workgroup"]) == (2, 2)
+    assert i["prep_workgroups"] == chunks * 2
     assert i["workgroups"] == len(lengths) * 4 * (dv // 32) and i["threads"] == 256
-    # its workspace is only the gated norm's f32 core output
+    # the workspace: per (chunk, k-head) q and k, per (chunk, v-head) W, U, Aqk and
+    # decay rows, f32; the gated norm adds its f32 core output
     d = dims(dk=dk, dv=dv)
-    assert ops.load().gdn_prefill_workspace_bytes(ctypes.byref(d), 3, 137) == 256
+    mc = 137 // clen + 3
+    floor = 4 * mc * (2 * 2 * clen * dk + 4 * (clen * dk + clen * dv + clen * clen + 3 * clen))
+    need = ops.load().gdn_prefill_workspace_bytes(ctypes.byref(d), 3, 137)
+    assert floor <= need <= floor + 16 * 256
     dn = dims(dk=dk, dv=dv, flags=ops.GATED_NORM)
-    assert ops.load().gdn_prefill_workspace_bytes(ctypes.byref(dn), 3, 137) >= 137 * 4 * dv * 4
+    assert ops.load().gdn_prefill_workspace_bytes(ctypes.byref(dn), 3, 137) >= need + 137 * 4 * dv * 4
     i = ops.prefill_launch_info(lengths, Hk=2, Hv=4, dk=128, dv=128, compute_units=256)
     assert i["carry_kind"] in (0, 1) and i["prep_workgroups"] > 0
