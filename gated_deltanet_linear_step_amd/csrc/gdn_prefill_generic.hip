@@ -16,15 +16,21 @@
 //  1. plan_generic_kernel -- the chunk table (several sequences only; one
 //     sequence's chunk bounds are closed-form).
 //  2. prep_generic_kernel -- per (chunk, k-head), all chunks in parallel: the
-//     normalised q and k rows, K K^T and Q K^T once, then for each v-head reading
-//     the k-head: gates and their prefix sums, A, T = (I + A)^-1 in 16 x 16
-//     blocks, W, U and scale * Aqk and the decay rows, all to the workspace.
+//     normalised q and k rows, the lower triangles of K K^T and Q K^T once, then
+//     for each v-head reading the k-head: gates and their prefix sums, A,
+//     T = (I + A)^-1 (16 x 16 diagonal blocks by substitution, the blocks below
+//     by block products), W, U, scale * Aqk, diag(e) K and the decay rows, all to
+//     the workspace.
 //  3. carry_generic_kernel -- per (sequence, v-head, 32 rows of dv), sequential
 //     over the sequence's chunks with the slice's f32 state resident in LDS: only
 //     the state-dependent products (Q S^T, W S^T, Aqk D, D^T diag(e) K). The next
 //     chunk's operands are loaded into registers while the current one runs.
 //  4. norm_generic_kernel -- the gated RMS norm of the f32 core output.
 // Chunks are 64 tokens, 32 when dk = 256 (the LDS then holds the 256-wide tiles).
+// LDS row pitches are chosen by how the MFMA operand reads index each array, so
+// that the 64 lanes of one read hit 64 different banks: an array whose row is
+// the lane's m or n index (lane % 16) takes a pitch of 4 or 36 mod 64, one whose
+// row is the contracted index (lane / 16) a pitch of 16 or 48 mod 64.
 
 #include "gdn_device.h"
 #include "gdn_kernels.h"
@@ -32,7 +38,6 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kSlice = 32;  // dv rows per carry workgroup
 
 template <int DK>
@@ -43,49 +48,140 @@ constexpr int gen_chunk()
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// C[m][n] = sum_k a(m, k) b(k, n) for m < M, n < N on v_mfma_f32_16x16x4_f32 (f32
-// operands, f32 accumulation). The 16 x 16 output tiles are dealt to the 4 waves,
-// two at a time so that consecutive products go to different accumulators; lane
-// (li, lg) = (lane % 16, lane / 16) feeds a(m0 + li, k0 + lg) and b(k0 + lg,
-// n0 + li) and receives C[m0 + 4 lg + r][n0 + li] in acc[r], handed to
-// c(m, n, value).
-template <int M, int N, int K, class FA, class FB, class FC>
-__device__ __forceinline__ void mfma_product(FA a, FB b, FC c)
+// One 16 x 16 tile of sum_k a(m, k) b(k, n) over k in [kb, kb + 4 KSTEPS) on
+// v_mfma_f32_16x16x4_f32, as two accumulator chains (alternate k-steps) added at
+// the end. Lane (li, lg) = (lane % 16, lane / 16) feeds a(m0 + li, k0 + lg) and
+// b(k0 + lg, n0 + li) and receives C[m0 + 4 lg + r][n0 + li] in element r.
+template <int KSTEPS, class FA, class FB>
+__device__ __forceinline__ f32x4 mfma_tile(FA a, FB b, int m0, int n0, int kb = 0)
 {
-    constexpr int TN = N / 16, NT = (M / 16) * TN;
-    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "16 x 16 x 4 tiles");
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    for (int t = wave; t < NT; t += 8) {
-        const int t2 = t + 4 < NT ? t + 4 : t;  // a second tile, or the first again
-        const int m0 = (t / TN) * 16, n0 = (t % TN) * 16, m1 = (t2 / TN) * 16, n1 = (t2 % TN) * 16;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int k0 = 0; k0 < K; k0 += 4) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m0 + li, k0 + lg), b(k0 + lg, n0 + li), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m1 + li, k0 + lg), b(k0 + lg, n1 + li), acc1, 0, 0, 0);
+    static_assert(KSTEPS % 2 == 0, "two chains");
+    // operands are read a block of BLK k-steps at a time, the next block's reads
+    // issued before this block's products
+    constexpr int BLK = KSTEPS < 16 ? KSTEPS : 16;
+    static_assert(KSTEPS % BLK == 0, "blocks");
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    float av[BLK], bv[BLK];
+#pragma unroll
+    for (int s = 0; s < BLK; ++s) {
+        av[s] = a(m0 + li, kb + 4 * s + lg);
+        bv[s] = b(kb + 4 * s + lg, n0 + li);
+    }
+    // keep the reads ahead of the products (the scheduler would otherwise sink
+    // each read next to its use and wait on it)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int blk = 0; blk < KSTEPS; blk += BLK) {
+        float an[BLK], bn[BLK];
+        if (blk + BLK < KSTEPS) {
+#pragma unroll
+            for (int s = 0; s < BLK; ++s) {
+                an[s] = a(m0 + li, kb + 4 * (blk + BLK + s) + lg);
+                bn[s] = b(kb + 4 * (blk + BLK + s) + lg, n0 + li);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            c(m0 + 4 * lg + r, n0 + li, acc0[r]);
-        if (t2 != t) {
+        for (int s = 0; s < BLK; s += 2) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s + 1], bv[s + 1], c1, 0, 0, 0);
+        }
+        if (blk + BLK < KSTEPS) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                c(m1 + 4 * lg + r, n1 + li, acc1[r]);
+            for (int s = 0; s < BLK; ++s) {
+                av[s] = an[s];
+                bv[s] = bn[s];
+            }
         }
     }
+    return c0 + c1;
+}
+
+// Two tiles that share the right operand, a1 b and a2 b over k in [kb, kb + 4
+// KSTEPS): one read of b serves both products; reads go a block ahead as above.
+template <int KSTEPS, class FA1, class FA2, class FB>
+__device__ __forceinline__ void mfma_tile2(FA1 a1, FA2 a2, FB b, int m0, int n0, int kb, f32x4 &r1, f32x4 &r2)
+{
+    constexpr int BLK = KSTEPS < 8 ? KSTEPS : 8;
+    static_assert(KSTEPS % BLK == 0 && BLK % 2 == 0, "blocks");
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, d0 = c0, d1 = c0;
+    float xv[BLK], yv[BLK], bv[BLK];
+#pragma unroll
+    for (int s = 0; s < BLK; ++s) {
+        const int k = kb + 4 * s + lg;
+        bv[s] = b(k, n0 + li);
+        xv[s] = a1(m0 + li, k);
+        yv[s] = a2(m0 + li, k);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int blk = 0; blk < KSTEPS; blk += BLK) {
+        float xn[BLK], yn[BLK], bn[BLK];
+        if (blk + BLK < KSTEPS) {
+#pragma unroll
+            for (int s = 0; s < BLK; ++s) {
+                const int k = kb + 4 * (blk + BLK + s) + lg;
+                bn[s] = b(k, n0 + li);
+                xn[s] = a1(m0 + li, k);
+                yn[s] = a2(m0 + li, k);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int s = 0; s < BLK; s += 2) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s], bv[s], c0, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(yv[s], bv[s], d0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s + 1], bv[s + 1], c1, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(yv[s + 1], bv[s + 1], d1, 0, 0, 0);
+        }
+        if (blk + BLK < KSTEPS) {
+#pragma unroll
+            for (int s = 0; s < BLK; ++s) {
+                xv[s] = xn[s];
+                yv[s] = yn[s];
+                bv[s] = bn[s];
+            }
+        }
+    }
+    r1 = c0 + c1;
+    r2 = d0 + d1;
+}
+
+// The same over k < m0 + 16: a product with a lower-triangular left operand
+// (zero for k > m), so output rows m0 .. m0 + 15 need only the first m0 + 16 k.
+template <int CC, class FA, class FB>
+__device__ __forceinline__ f32x4 mfma_tile_lower(FA a, FB b, int m0, int n0)
+{
+    switch (m0 >> 4) {
+    case 0:
+        return mfma_tile<4>(a, b, m0, n0);
+    case 1:
+        return mfma_tile<8>(a, b, m0, n0);
+    case 2:
+        if constexpr (CC > 32)
+            return mfma_tile<12>(a, b, m0, n0);
+        break;
+    default:
+        if constexpr (CC > 32)
+            return mfma_tile<16>(a, b, m0, n0);
+        break;
+    }
+    return f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ---------------------------------------------------------------- workspace
 
 struct GenWs {
-    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, q, k, w, u, aq, dec, onorm, total;
+    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, q, ke, w, u, aq, dec, onorm, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // MC = the chunk count bound (total / chunk + N); per (chunk, k-head) the
-// normalised q and k rows, per (chunk, v-head) W, U, scale * Aqk and three decay
-// rows, all f32; with the gated norm an f32 core output.
+// normalised q rows, per (chunk, v-head) diag(e) K, W, U, scale * Aqk and three
+// decay rows, all f32; with the gated norm an f32 core output.
 GenWs gen_layout(int Hk, int Hv, int dk, int dv, int64_t MC, int N, int64_t total, bool norm)
 {
     const int C = dk >= 256 ? 32 : 64;
@@ -101,7 +197,7 @@ GenWs gen_layout(int Hk, int Hv, int dk, int dv, int64_t MC, int N, int64_t tota
     L.chunk_len = take(sizeof(int32_t) * MC);
     L.seq_chunk0 = take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     L.q = take(sizeof(float) * MC * Hk * C * dk);
-    L.k = take(sizeof(float) * MC * Hk * C * dk);
+    L.ke = take(sizeof(float) * MC * Hv * C * dk);
     L.w = take(sizeof(float) * MC * Hv * C * dk);
     L.u = take(sizeof(float) * MC * Hv * C * dv);
     L.aq = take(sizeof(float) * MC * Hv * C * C);
@@ -164,23 +260,32 @@ __global__ __launch_bounds__(256) void plan_generic_kernel(PrefillParams p)
 
 // ---------------------------------------------------------------- 2. prep
 
+constexpr int kPrepThreads = 512;  // 8 waves
+
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams p)
+__global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void prep_generic_kernel(
+    PrefillParams p)
 {
     constexpr int CC = gen_chunk<DK>();
-    constexpr int KP = DK + 1, CP = CC + 1, VP = kSlice + 1;
-    constexpr int NB = CC / 16;
-    static_assert(DV % kSlice == 0 && CC <= 64 && CC % 16 == 0 && DK % 16 == 0, "shape");
+    constexpr int NT = kPrepThreads, NW = NT / 64, NB = CC / 16;
+    // v columns staged in LDS per pass
+    constexpr int VSL = (CC == 64 && DK >= 128) ? 64 : (DV < 128 ? DV : 128);
+    constexpr int PA = DK + 2, PB = DK + 16, PC = CC + 2, PG = CC + 4, PV = VSL + 16;
+    constexpr int PQB = PA > PB ? PA : PB;
+    static_assert(DV % VSL == 0 && CC % 16 == 0 && DK % 16 == 0 && CC * CC % NT == 0 && CC * DK % NT == 0 &&
+                      CC * VSL % NT == 0 && CC % NW == 0 && NB - 1 <= NW,
+                  "shape");
 
-    __shared__ float Kc[CC][KP];  // the chunk's (normalised) keys
-    __shared__ float Qc[CC][KP];  // its queries
-    __shared__ float Gm[CC][CP];  // K K^T
-    __shared__ float Qk[CC][CP];  // Q K^T
-    __shared__ float Am[CC][CP];  // A (strictly lower), per v-head
-    __shared__ float Tm[CC][CP];  // T = (I + A)^-1
-    __shared__ float Vs[CC][VP];  // one 32-wide slice of v
-    __shared__ float Mb[NB > 1 ? NB - 1 : 1][16][16];  // block sums of the inverse
-    __shared__ float G_s[CC], beta_s[CC], bg_s[CC];
+    __shared__ float Kc[CC][PA];     // the chunk's normalised keys
+    __shared__ float QKb[CC * PQB];  // its normalised queries [CC][PA], then diag(beta gamma) K [CC][PB]
+    __shared__ float Gm[CC][PG];     // K K^T (lower triangle of 16 x 16 tiles)
+    __shared__ float Qk[CC][PG];     // Q K^T (same)
+    __shared__ float Am[CC][PC];     // A (strictly lower), per v-head
+    __shared__ float Tm[CC][PC];     // T = (I + A)^-1
+    __shared__ float Vb[CC][PV];     // diag(beta) V, VSL columns
+    __shared__ float G_s[CC], beta_s[CC], bg_s[CC], e_s[CC];
+    auto Qc = [&](int r, int c) -> float & { return QKb[r * PA + c]; };
+    auto Kb = [&](int r, int c) -> float & { return QKb[r * PB + c]; };
 
     const HeadCfg &hc = p.hc;
     const ActInputs &in = p.in;
@@ -189,24 +294,38 @@ __global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams
     const bool one_seq = p.N == 1;  // tokens [0, total): no table
     const int64_t tok0 = one_seq ? (int64_t)CC * chunk : p.chunk_start[chunk];
     const int n = one_seq ? min(CC, p.total - CC * chunk) : p.chunk_len[chunk];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
     const uint32_t flags = hc.flags;
     const bool raw = flags & F_RAW_GATES;
     const int qdt = in.qkv_dt;
     auto vhead = [&](int j) { return hc.head_map == 0 ? kh * G + j : kh + j * Hk; };
+    const void *gsa = raw ? in.a : static_cast<const void *>(in.g);
+    const void *gsb = raw ? in.b : static_cast<const void *>(in.beta);
+    const int gdt = raw ? in.ab_dt : DT_F32;
+
+    // the gate words of one v-head (wave 0, lane = token), loaded a v-head ahead
+    GateWord ga{0u}, gb{0u};
+    auto load_gates = [&](int j) {
+        const int64_t gi = (tok0 + min(lane, n - 1)) * Hv + vhead(j);
+        ga = load_gate(gsa, gi, gdt);
+        gb = load_gate(gsb, gi, gdt);
+    };
+    if (wave == 0)
+        load_gates(0);
 
     // -- keys and queries: every load issued before any use, no branch around a
     // load (rows past the chunk's end re-read row n-1, columns past dk re-read
     // column dk-1, both masked after; the 32-bit word holding each element -- a
     // q/k row has an even length from a 4-element aligned start, so the word stays
-    // in the row -- and the dtype by a select). Wave w takes rows w, w + 4, ...;
+    // in the row -- and the dtype by a select). Wave w takes rows w, w + 8, ...;
     // lane l columns l, l + 64, ...
     {
-        constexpr int RW = CC / 4, EPL = (DK + 63) / 64;
+        constexpr int RW = CC / NW, EPL = (DK + 63) / 64;
         uint32_t kw[RW][EPL], qw[RW][EPL];
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
-            const int64_t row = tok0 + min(wave + 4 * i, n - 1);
+            const int64_t row = tok0 + min(wave + NW * i, n - 1);
 #pragma unroll
             for (int m = 0; m < EPL; ++m) {
                 const int c = min(lane + 64 * m, DK - 1);
@@ -215,10 +334,9 @@ __global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams
             }
         }
         float *gq = p.gq + ((int64_t)chunk * Hk + kh) * CC * DK;
-        float *gk = p.gk + ((int64_t)chunk * Hk + kh) * CC * DK;
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
-            const int r = wave + 4 * i;
+            const int r = wave + NW * i;
             float kv[EPL], qv[EPL];
             float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -241,8 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams
                 const int c = lane + 64 * m;
                 if (c < DK) {
                     Kc[r][c] = kv[m] * ik;
-                    Qc[r][c] = qv[m] * iq;
-                    gk[r * DK + c] = kv[m] * ik;
+                    Qc(r, c) = qv[m] * iq;
                     gq[r * DK + c] = qv[m] * iq;
                 }
             }
@@ -250,25 +367,50 @@ __global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams
     }
     __syncthreads();
 
-    // -- K K^T and Q K^T, shared by the v-heads reading this k-head
-    mfma_product<CC, CC, DK>([&](int t, int i) { return Kc[t][i]; }, [&](int i, int s) { return Kc[s][i]; },
-                             [&](int t, int s, float v) { Gm[t][s] = v; });
-    mfma_product<CC, CC, DK>([&](int t, int i) { return Qc[t][i]; }, [&](int i, int s) { return Kc[s][i]; },
-                             [&](int t, int s, float v) { Qk[t][s] = v; });
+    // -- K K^T and Q K^T on the 16 x 16 tiles on and below the diagonal (A and
+    // Aqk are lower triangular), one read of the keys for both
+    {
+        constexpr int NTRI = NB * (NB + 1) / 2;
+        for (int u = wave; u < NTRI; u += NW) {
+            int tm = 0, tn = u;  // u = tm (tm + 1) / 2 + tn, tn <= tm
+            while (tn > tm) {
+                tn -= tm + 1;
+                ++tm;
+            }
+            const int m0 = 16 * tm, n0 = 16 * tn;
+            f32x4 ga, qa;
+            mfma_tile2<DK / 4>([&](int t, int i) { return Kc[t][i]; }, [&](int t, int i) { return Qc(t, i); },
+                               [&](int i, int s2) { return Kc[s2][i]; }, m0, n0, 0, ga, qa);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Gm[m0 + 4 * lg + r][n0 + li] = ga[r];
+                Qk[m0 + 4 * lg + r][n0 + li] = qa[r];
+            }
+        }
+    }
 
-    const void *gsa = raw ? in.a : static_cast<const void *>(in.g);
-    const void *gsb = raw ? in.b : static_cast<const void *>(in.beta);
-    const int gdt = raw ? in.ab_dt : DT_F32;
+    constexpr int VPT = CC * VSL / NT;
+    uint32_t vw[VPT];
     for (int j = 0; j < G; ++j) {
         const int h = vhead(j);
+        // this v-head's first VSL columns of v, in flight from here
+        auto load_v = [&](int d0) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int e = tid + NT * i;
+                const int64_t row = tok0 + min(e / VSL, n - 1);
+                vw[i] = load_word_nb(in.v, row * in.v_stride + (int64_t)h * DV + d0 + e % VSL, qdt);
+            }
+        };
+        load_v(0);
         __syncthreads();  // the products are in LDS; the previous v-head is done with its buffers
         // -- gates and their in-chunk prefix sums (wave 0, lane = token); tokens
         // past the chunk's end get g = beta = 0, so they carry G_{n-1}
         float *dec = p.gdec + ((int64_t)chunk * Hv + h) * 3 * CC;
         if (wave == 0) {
-            const int64_t gi = (tok0 + min(lane, n - 1)) * Hv + h;
-            const GateWord ga = load_gate(gsa, gi, gdt), gb = load_gate(gsb, gi, gdt);
             float g = gate_value(ga, gdt), beta = gate_value(gb, gdt);
+            if (j + 1 < G)
+                load_gates(j + 1);
             if (raw) {
                 const float rate = hc.decay_kind == 0 ? -expf(in.decay_param[h]) : in.decay_param[h];
                 g = rate * softplus_f(g + in.dt_bias[h]);
@@ -285,23 +427,37 @@ __global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams
             }
             const float Glast = __shfl(Gc, CC - 1, 64);
             if (lane < CC) {
-                const float gam = expf(Gc);
+                const float gam = expf(Gc), ed = expf(Glast - Gc);
                 G_s[lane] = Gc;
                 beta_s[lane] = beta;
                 bg_s[lane] = beta * gam;
-                dec[lane] = hc.scale * gam;         // the output's decay (scale folded in)
-                dec[CC + lane] = expf(Glast - Gc);  // the state update's decay
-                dec[2 * CC + lane] = gam;           // gamma_t (gamma_last at CC - 1)
+                e_s[lane] = ed;
+                dec[lane] = hc.scale * gam;  // the output's decay (scale folded in)
+                dec[CC + lane] = ed;         // the state update's decay
+                dec[2 * CC + lane] = gam;    // gamma_t (gamma_last at CC - 1)
             }
         }
         __syncthreads();
-        // -- A and scale * Aqk (to the workspace)
-        float *aq = p.gaq + ((int64_t)chunk * Hv + h) * CC * CC;
-        for (int e = tid; e < CC * CC; e += kThreads) {
-            const int t = e / CC, s = e % CC;
-            const float dg = s <= t ? expf(G_s[t] - G_s[s]) : 0.f;
-            Am[t][s] = s < t ? beta_s[t] * dg * Gm[t][s] : 0.f;
-            aq[e] = hc.scale * dg * Qk[t][s];
+        // -- A and scale * Aqk (to the workspace); diag(beta gamma) K for W and
+        // diag(e) K (to the workspace) for the state update. Only the tiles on and
+        // below the diagonal of K K^T and Q K^T were computed: select, not scale.
+        {
+            float *aq = p.gaq + ((int64_t)chunk * Hv + h) * CC * CC;
+#pragma unroll
+            for (int i = 0; i < CC * CC / NT; ++i) {
+                const int e = tid + NT * i, t = e / CC, s2 = e % CC;
+                const float dg = s2 <= t ? expf(G_s[t] - G_s[s2]) : 0.f;
+                Am[t][s2] = s2 < t ? beta_s[t] * dg * Gm[t][s2] : 0.f;
+                aq[e] = s2 <= t ? hc.scale * dg * Qk[t][s2] : 0.f;
+            }
+            float *ke = p.gke + ((int64_t)chunk * Hv + h) * CC * DK;
+#pragma unroll
+            for (int i = 0; i < CC * DK / NT; ++i) {
+                const int e = tid + NT * i, t = e / DK, c = e % DK;
+                const float kv = Kc[t][c];
+                Kb(t, c) = bg_s[t] * kv;
+                ke[e] = e_s[t] * kv;
+            }
         }
         __syncthreads();
         // -- T = (I + A)^-1 (unit lower triangular), in 16 x 16 blocks. (a) Each
@@ -325,90 +481,126 @@ __global__ __launch_bounds__(kThreads, 1) void prep_generic_kernel(PrefillParams
                 Tm[r][b0 + c] = 0.f;
         }
         __syncthreads();
-        // (b) the blocks below the diagonal, one sub-diagonal after another:
-        // T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj)
+        // (b) the blocks below the diagonal, one sub-diagonal after another, a wave
+        // per block: T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj). The inner sum M
+        // stays in the accumulator; the product with T_ii then pairs k-step kk and
+        // row-of-four lg with contraction index 4 lg + kk, the row of M that the
+        // lane holds in element kk.
         for (int L = 1; L < NB; ++L) {
-            for (int e = tid; e < (NB - L) * 256; e += kThreads) {
-                const int jb = e >> 8, i = jb + L, r = (e >> 4) & 15, c = e & 15;
-                float acc = 0.f;
-                for (int kb = jb; kb < i; ++kb) {
-                    float part = 0.f;  // one 16-long block: loads issued together
+            if (wave < NB - L) {
+                const int jb = wave, ib = wave + L;
+                f32x4 m = {0.f, 0.f, 0.f, 0.f};
+                for (int kb = jb; kb < ib; ++kb) {
 #pragma unroll
-                    for (int s2 = 0; s2 < 16; ++s2)
-                        part = fmaf(Am[16 * i + r][16 * kb + s2], Tm[16 * kb + s2][16 * jb + c], part);
-                    acc += part;
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int k = 16 * kb + 4 * kk + lg;
+                        m = __builtin_amdgcn_mfma_f32_16x16x4f32(Am[16 * ib + li][k], Tm[k][16 * jb + li], m, 0, 0,
+                                                                 0);
+                    }
                 }
-                Mb[jb][r][c] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < (NB - L) * 256; e += kThreads) {
-                const int jb = e >> 8, i = jb + L, r = (e >> 4) & 15, c = e & 15;
-                float acc = 0.f;
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s2 = 0; s2 < 16; ++s2)
-                    acc = fmaf(Tm[16 * i + r][16 * i + s2], Mb[jb][s2][c], acc);
-                Tm[16 * i + r][16 * jb + c] = -acc;
+                for (int kk = 0; kk < 4; ++kk)
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[16 * ib + li][16 * ib + 4 * lg + kk], m[kk], t, 0,
+                                                             0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Tm[16 * ib + 4 * lg + r][16 * jb + li] = -t[r];
             }
             __syncthreads();
         }
-        // -- W = T diag(beta gamma) K (to the workspace)
+        // -- W = T diag(beta gamma) K and U = T diag(beta) V (to the workspace), v
+        // staged VSL columns at a time; T is lower triangular, so each output row
+        // block contracts over the chunk's first m0 + 16 tokens only (longest first)
         float *wg = p.gw + ((int64_t)chunk * Hv + h) * CC * DK;
-        mfma_product<CC, DK, CC>([&](int t, int s) { return Tm[t][s] * bg_s[s]; },
-                                 [&](int s, int i) { return Kc[s][i]; },
-                                 [&](int t, int i, float v) { wg[t * DK + i] = v; });
-        // -- U = T diag(beta) V (to the workspace), 32 columns of v at a time
         float *ug = p.gu + ((int64_t)chunk * Hv + h) * CC * DV;
-        for (int d0 = 0; d0 < DV; d0 += kSlice) {
-            constexpr int VPT = CC * kSlice / kThreads;
-            uint32_t vw[VPT];
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int e = tid + kThreads * i;
-                const int64_t row = tok0 + min(e / kSlice, n - 1);
-                vw[i] = load_word_nb(in.v, row * in.v_stride + (int64_t)h * DV + d0 + e % kSlice, qdt);
+        constexpr int NWT = NB * (DK / 16), NUT = NB * (VSL / 16);
+        for (int d0 = 0; d0 < DV; d0 += VSL) {
+            if (d0 > 0) {
+                load_v(d0);
+                __syncthreads();  // the previous pass is done with Vb
             }
-            __syncthreads();  // the previous slice's product is done with Vs
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int e = tid + kThreads * i, r = e / kSlice, jj = e % kSlice;
-                Vs[r][jj] = r < n ? word_to_f32(vw[i], jj, qdt) : 0.f;
+                const int e = tid + NT * i, r = e / VSL, jj = e % VSL;
+                Vb[r][jj] = r < n ? beta_s[r] * word_to_f32(vw[i], jj, qdt) : 0.f;
             }
             __syncthreads();
-            mfma_product<CC, kSlice, CC>([&](int t, int s) { return Tm[t][s] * beta_s[s]; },
-                                         [&](int s, int jj) { return Vs[s][jj]; },
-                                         [&](int t, int jj, float v) { ug[t * DV + d0 + jj] = v; });
+            const int first = d0 == 0 ? 0 : NWT;
+            for (int u = first + wave; u < NWT + NUT; u += NW) {
+                if (u < NWT) {
+                    const int m0 = (NB - 1 - u / (DK / 16)) * 16, n0 = (u % (DK / 16)) * 16;
+                    const f32x4 acc = mfma_tile_lower<CC>([&](int t, int s2) { return Tm[t][s2]; },
+                                                          [&](int s2, int i) { return Kb(s2, i); }, m0, n0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        wg[(m0 + 4 * lg + r) * DK + n0 + li] = acc[r];
+                } else {
+                    const int v = u - NWT;
+                    const int m0 = (NB - 1 - v / (VSL / 16)) * 16, n0 = (v % (VSL / 16)) * 16;
+                    const f32x4 acc = mfma_tile_lower<CC>([&](int t, int s2) { return Tm[t][s2]; },
+                                                          [&](int s2, int jj) { return Vb[s2][jj]; }, m0, n0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ug[(m0 + 4 * lg + r) * DV + d0 + n0 + li] = acc[r];
+                }
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------- 3. carry
 
+constexpr int kCarryThreads = 512;  // 8 waves, two per SIMD
+
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void carry_generic_kernel(PrefillParams p)
+__global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void carry_generic_kernel(
+    PrefillParams p)
 {
     constexpr int CC = gen_chunk<DK>();
-    constexpr int KP = DK + 1, CP = CC + 1, VP = kSlice + 1;
+    constexpr int NT = kCarryThreads, NW = NT / 64;
+    // Row pitches (floats) chosen by how the MFMA operand reads index each array,
+    // so that the 64 lanes of one read hit 64 different banks: arrays whose row is
+    // the lane's m or n index (lane % 16) take a pitch of 4 or 36 mod 64 (Ss, Qn,
+    // Wm, Aq, Qs); arrays whose row is the contracted index (lane / 16) a pitch of
+    // 16 or 48 mod 64 (Kn, Us).
+    constexpr int PA = DK + 2, PK = DK + 16, PC = CC + 2, PU = kSlice + 16, PQ = kSlice + 4;
     constexpr int NSL = DV / kSlice;
     // per thread: the words of one chunk's operands it moves into LDS
-    constexpr int WQK = CC * DK / kThreads, WU = CC * kSlice / kThreads, WA = CC * CC / kThreads;
-    static_assert(CC * DK % kThreads == 0 && CC * kSlice % kThreads == 0 && CC * CC % kThreads == 0 &&
-                      3 * CC <= kThreads, "operand split");
+    constexpr int WQK = CC * DK / NT, WU = CC * kSlice / NT, WA = CC * CC / NT;
+    // Q S^T and W S^T: NT1 tiles of 16 x 16; with fewer tiles than waves the
+    // contraction over dk is split KS ways and the parts summed through LDS
+    constexpr int NT1 = (CC / 16) * (kSlice / 16), KS = NW / NT1;
+    // the output and the state update: NO + NU tiles, all contracting over the chunk
+    constexpr int NO = (CC / 16) * (kSlice / 16), NU = (kSlice / 16) * (DK / 16);
+    static_assert(CC * DK % NT == 0 && CC * kSlice % NT == 0 && CC * CC % NT == 0 && 3 * CC <= NT,
+                  "operand split");
+    static_assert(NT1 <= NW && NW % NT1 == 0 && (DK / KS) % 8 == 0, "phase-1 tiles");
 
-    __shared__ float Ss[kSlice][KP];  // the state slice S[dv0 + j][i]
-    __shared__ float Qn[CC][KP];      // normalised q rows
-    __shared__ float Kn[CC][KP];      // normalised k rows
-    __shared__ float Wm[CC][KP];      // W
-    __shared__ float Us[CC][VP];      // U of the slice, then D
-    __shared__ float Aq[CC][CP];      // scale * Aqk
-    __shared__ float Qs[CC][VP];      // Q S^T
+    __shared__ float Ss[kSlice][PA];  // the state slice S[dv0 + j][i]
+    __shared__ float Qn[CC][PA];      // normalised q rows
+    __shared__ float Wm[CC][PA];      // W
+    __shared__ float Kn[CC][PK];      // exp(G_last - G_t) k_t
+    __shared__ float Us[CC][PU];      // U of the slice, then D = U - W S^T
+    __shared__ float Aq[CC][PC];      // scale * Aqk
+    __shared__ float Qs[CC][PQ];      // scale gamma_t (Q S^T)_t
     __shared__ float Dc[3][CC];       // scale gamma_t, exp(G_last - G_t), gamma_t
+    __shared__ float Pq[KS > 1 ? KS - 1 : 1][KS > 1 ? CC : 1][PQ];  // split-k parts
+    __shared__ float Pw[KS > 1 ? KS - 1 : 1][KS > 1 ? CC : 1][PQ];
 
     const HeadCfg &hc = p.hc;
-    const int Hv = hc.Hv, Hk = hc.Hk;
-    const int slice = blockIdx.x % NSL;
-    const int h = (blockIdx.x / NSL) % Hv;
-    const int seq = blockIdx.x / (NSL * Hv);
-    const int kh = k_head_of(hc.head_map, h, Hk, Hv);
+    const int Hv = hc.Hv, Hk = hc.Hk, G = Hv / Hk;
+    // Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the 8 XCDs
+    // in turn). Each XCD takes a contiguous range of (sequence, k-head, v-head of
+    // that k-head, slice), so the slices of one v-head, and the v-heads of one
+    // k-head, read the chunk's q, k and W through the same L2.
+    const int nwg = (int)gridDim.x;
+    const int L = nwg % 8 == 0 ? (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int slice = L % NSL;
+    const int jv = (L / NSL) % G;
+    const int kh = (L / (NSL * G)) % Hk;
+    const int seq = L / (NSL * Hv);
+    const int h = hc.head_map == 0 ? kh * G + jv : kh + jv * Hk;
     const int dv0 = slice * kSlice;
     const bool one_seq = p.N == 1;
     const int start = one_seq ? 0 : p.cu[seq];
@@ -417,35 +609,38 @@ __global__ __launch_bounds__(kThreads, 1) void carry_generic_kernel(PrefillParam
         return;  // empty sequence: state untouched
     const int nch = (len + CC - 1) / CC;
     const int cfirst = one_seq ? 0 : p.seq_chunk0[seq];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
     const uint32_t flags = hc.flags;
     float *Sg = p.state + (((int64_t)seq * Hv + h) * DV + dv0) * DK;
+    void *obase = (flags & F_GATED_NORM) ? static_cast<void *>(p.onorm) : p.out;
+    const int odt = (flags & F_GATED_NORM) ? DT_F32 : p.out_dt;
 
-    for (int e = tid; e < kSlice * DK; e += kThreads)
+    for (int e = tid; e < kSlice * DK; e += NT)
         Ss[e / DK][e % DK] = Sg[e];
 
-    // the operands of one chunk, as registers: element tid + 256 i of each array
+    // the operands of one chunk, as registers: element tid + NT i of each array
     float rq[WQK], rk[WQK], rw[WQK], ru[WU], ra[WA], rd;
     auto fetch = [&](int ci) {
         const int64_t c = cfirst + ci;
-        const float *gq = p.gq + (c * Hk + kh) * CC * DK, *gk = p.gk + (c * Hk + kh) * CC * DK;
+        const float *gq = p.gq + (c * Hk + kh) * CC * DK, *gk = p.gke + (c * Hv + h) * CC * DK;
         const float *gw = p.gw + (c * Hv + h) * CC * DK;
         const float *gu = p.gu + (c * Hv + h) * CC * DV + dv0;
         const float *ga = p.gaq + (c * Hv + h) * CC * CC, *gd = p.gdec + (c * Hv + h) * 3 * CC;
 #pragma unroll
         for (int i = 0; i < WQK; ++i) {
-            rq[i] = gq[tid + kThreads * i];
-            rk[i] = gk[tid + kThreads * i];
-            rw[i] = gw[tid + kThreads * i];
+            rq[i] = gq[tid + NT * i];
+            rk[i] = gk[tid + NT * i];
+            rw[i] = gw[tid + NT * i];
         }
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
-            const int e = tid + kThreads * i;
+            const int e = tid + NT * i;
             ru[i] = gu[(e / kSlice) * DV + e % kSlice];
         }
 #pragma unroll
         for (int i = 0; i < WA; ++i)
-            ra[i] = ga[tid + kThreads * i];
+            ra[i] = ga[tid + NT * i];
         rd = gd[min(tid, 3 * CC - 1)];
     };
     fetch(0);
@@ -456,19 +651,19 @@ __global__ __launch_bounds__(kThreads, 1) void carry_generic_kernel(PrefillParam
         __syncthreads();  // the previous chunk is done with every buffer
 #pragma unroll
         for (int i = 0; i < WQK; ++i) {
-            const int e = tid + kThreads * i;
+            const int e = tid + NT * i;
             Qn[e / DK][e % DK] = rq[i];
             Kn[e / DK][e % DK] = rk[i];
             Wm[e / DK][e % DK] = rw[i];
         }
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
-            const int e = tid + kThreads * i;
+            const int e = tid + NT * i;
             Us[e / kSlice][e % kSlice] = ru[i];
         }
 #pragma unroll
         for (int i = 0; i < WA; ++i) {
-            const int e = tid + kThreads * i;
+            const int e = tid + NT * i;
             Aq[e / CC][e % CC] = ra[i];
         }
         if (tid < 3 * CC)
@@ -477,33 +672,73 @@ __global__ __launch_bounds__(kThreads, 1) void carry_generic_kernel(PrefillParam
             fetch(ci + 1);  // the next chunk's operands, in flight from here
         __syncthreads();
 
-        // -- Q S^T and D = U - W S^T, both on the entering state
-        mfma_product<CC, kSlice, DK>([&](int t, int i) { return Qn[t][i]; }, [&](int i, int j) { return Ss[j][i]; },
-                                     [&](int t, int j, float v) { Qs[t][j] = v; });
-        mfma_product<CC, kSlice, DK>([&](int t, int i) { return Wm[t][i]; }, [&](int i, int j) { return Ss[j][i]; },
-                                     [&](int t, int j, float v) { Us[t][j] -= v; });
-        __syncthreads();
-
-        // -- O = scale gamma Q S^T + (scale Aqk) D to the output, and the state
-        // update S <- gamma_last S + D^T diag(e) K (separate buffers: no barrier)
+        // -- Q S^T and W S^T on the entering state, one read of S for both;
+        // Qs = scale gamma_t (Q S^T), Us = D = U - W S^T
         {
-            void *obase = (flags & F_GATED_NORM) ? static_cast<void *>(p.onorm) : p.out;
-            const int odt = (flags & F_GATED_NORM) ? DT_F32 : p.out_dt;
-            mfma_product<CC, kSlice, CC>([&](int t, int s) { return Aq[t][s]; },
-                                         [&](int s, int j) { return Us[s][j]; },
-                                         [&](int t, int j, float v) {
-                                             if (t < n)
-                                                 store_act(obase, ((tok0 + t) * Hv + h) * DV + dv0 + j, odt,
-                                                           fmaf(Dc[0][t], Qs[t][j], v));
-                                         });
-            const float gl = Dc[2][CC - 1];
-            mfma_product<kSlice, DK, CC>([&](int j, int t) { return Us[t][j] * Dc[1][t]; },
-                                         [&](int t, int i) { return Kn[t][i]; },
-                                         [&](int j, int i, float v) { Ss[j][i] = fmaf(gl, Ss[j][i], v); });
+            const int tile = wave % NT1, part = wave / NT1;
+            const int m0 = (tile / (kSlice / 16)) * 16, n0 = (tile % (kSlice / 16)) * 16;
+            f32x4 qa, wa;
+            mfma_tile2<DK / KS / 4>([&](int t, int i) { return Qn[t][i]; }, [&](int t, int i) { return Wm[t][i]; },
+                                    [&](int i, int j) { return Ss[j][i]; }, m0, n0, part * (DK / KS), qa, wa);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = m0 + 4 * lg + r, j = n0 + li;
+                if (part == 0) {
+                    Qs[t][j] = Dc[0][t] * qa[r];
+                    Us[t][j] -= wa[r];
+                } else {
+                    Pq[part - 1][t][j] = qa[r];
+                    Pw[part - 1][t][j] = wa[r];
+                }
+            }
+        }
+        __syncthreads();
+        if (KS > 1) {  // add the other parts of the split contraction
+            for (int e = tid; e < CC * kSlice; e += NT) {
+                const int t = e / kSlice, j = e % kSlice;
+                float sq = 0.f, sw = 0.f;
+#pragma unroll
+                for (int q = 0; q < KS - 1; ++q) {
+                    sq += Pq[q][t][j];
+                    sw += Pw[q][t][j];
+                }
+                Qs[t][j] = fmaf(Dc[0][t], sq, Qs[t][j]);
+                Us[t][j] -= sw;
+            }
+            __syncthreads();
+        }
+
+        // -- the state update S <- gamma_last S + D^T diag(e) K and the output
+        // O = Qs + (scale Aqk) D, as one list of tiles: the update's first, then the
+        // output's from the longest contraction down (Aqk is zero above the
+        // diagonal, so output rows m0 .. m0 + 15 contract over the first m0 + 16)
+        const float gl = Dc[2][CC - 1];
+        for (int u = wave; u < NU + NO; u += NW) {
+            if (u < NU) {
+                const int m0 = (u % (kSlice / 16)) * 16, n0 = (u / (kSlice / 16)) * 16;
+                const f32x4 acc = mfma_tile<CC / 4>([&](int j, int t) { return Us[t][j]; },
+                                                    [&](int t, int i) { return Kn[t][i]; }, m0, n0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = m0 + 4 * lg + r, i = n0 + li;
+                    Ss[j][i] = fmaf(gl, Ss[j][i], acc[r]);
+                }
+            } else {
+                const int o = u - NU;
+                const int m0 = (CC / 16 - 1 - o / (kSlice / 16)) * 16, n0 = (o % (kSlice / 16)) * 16;
+                const f32x4 acc = mfma_tile_lower<CC>([&](int t, int s) { return Aq[t][s]; },
+                                                      [&](int s, int j) { return Us[s][j]; }, m0, n0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = m0 + 4 * lg + r, j = n0 + li;
+                    if (t < n)
+                        store_act(obase, ((tok0 + t) * Hv + h) * DV + dv0 + j, odt, Qs[t][j] + acc[r]);
+                }
+            }
         }
     }
     __syncthreads();
-    for (int e = tid; e < kSlice * DK; e += kThreads)
+    for (int e = tid; e < kSlice * DK; e += NT)
         Sg[e] = Ss[e / DK][e % DK];
 }
 
@@ -543,9 +778,9 @@ hipError_t launch_generic(const PrefillParams &p, hipStream_t s)
     if (p.N > 1)
         hipLaunchKernelGGL((plan_generic_kernel<gen_chunk<DK>()>), dim3(1), dim3(256), 0, s, p);
     hipLaunchKernelGGL((prep_generic_kernel<DK, DV>), dim3((unsigned)((int64_t)p.num_chunks * p.hc.Hk)),
-                       dim3(kThreads), 0, s, p);
+                       dim3(kPrepThreads), 0, s, p);
     hipLaunchKernelGGL((carry_generic_kernel<DK, DV>), dim3((unsigned)((int64_t)p.N * p.hc.Hv * (DV / kSlice))),
-                       dim3(kThreads), 0, s, p);
+                       dim3(kCarryThreads), 0, s, p);
     if (p.hc.flags & F_GATED_NORM) {
         const int64_t rows = (int64_t)p.total * p.hc.Hv;
         hipLaunchKernelGGL((norm_generic_kernel<DV>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
@@ -582,7 +817,7 @@ void prefill_generic_carve(PrefillParams &p, void *ws, int64_t max_chunks)
     p.chunk_len = reinterpret_cast<int32_t *>(b + L.chunk_len);
     p.seq_chunk0 = reinterpret_cast<int32_t *>(b + L.seq_chunk0);
     p.gq = reinterpret_cast<float *>(b + L.q);
-    p.gk = reinterpret_cast<float *>(b + L.k);
+    p.gke = reinterpret_cast<float *>(b + L.ke);
     p.gw = reinterpret_cast<float *>(b + L.w);
     p.gu = reinterpret_cast<float *>(b + L.u);
     p.gaq = reinterpret_cast<float *>(b + L.aq);

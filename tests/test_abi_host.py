@@ -328,11 +328,11 @@ def test_prefill_other_head_shapes_take_the_one_kernel_path(dk, dv):
     assert (i["carry_kind"], i["slices_per_workgroup"]) == (2, 2)
     assert i["prep_workgroups"] == chunks * 2
     assert i["workgroups"] == len(lengths) * 4 * (dv // 32) and i["threads"] == 256
-    # the workspace: per (chunk, k-head) q and k, per (chunk, v-head) W, U, Aqk and
-    # decay rows, f32; the gated norm adds its f32 core output
+    # the workspace: per (chunk, k-head) q, per (chunk, v-head) diag(e) K, W, U,
+    # Aqk and decay rows, f32; the gated norm adds its f32 core output
     d = dims(dk=dk, dv=dv)
     mc = 137 // clen + 3
-    floor = 4 * mc * (2 * 2 * clen * dk + 4 * (clen * dk + clen * dv + clen * clen + 3 * clen))
+    floor = 4 * mc * (2 * clen * dk + 4 * (2 * clen * dk + clen * dv + clen * clen + 3 * clen))
     need = ops.load().gdn_prefill_workspace_bytes(ctypes.byref(d), 3, 137)
     assert floor <= need <= floor + 16 * 256
     dn = dims(dk=dk, dv=dv, flags=ops.GATED_NORM)
