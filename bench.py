@@ -261,7 +261,9 @@ HEAD_SHAPES = ((32, 32), (64, 64), (96, 96), (128, 128), (64, 128), (128, 64), (
 def head_shapes_bench(torch, ops, synth, calls=300, warmup=30):
     """The fused decode layer at every built (dk, dv) head shape: B=64 x 1 token,
     Hk=16, Hv=32, tiled map, bf16 N(0,1) activations, fp32 state; state GB/s over
-    back-to-back launches (the state is read and written once per launch)."""
+    back-to-back launches (the state is read and written once per launch), without
+    and with the GDN_STREAM_STATE hint (the hint is meant for states that do not
+    stay in the 256 MB Infinity Cache: here 128x256, 256x128 and 256x256)."""
     dev = torch.device("cuda:0")
     B, Hk, Hv = 64, 16, 32
     res = {}
@@ -272,28 +274,35 @@ def head_shapes_bench(torch, ops, synth, calls=300, warmup=30):
         cb = torch.empty_like(S["conv_state"])
         out = torch.empty((B, Hv, dv), dtype=torch.bfloat16, device=dev)
         x, QK = S["x"], Hk * dk
-        calls_ = [ops.prepare_decode_layer(
-            x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:], S["state"], S["conv_w"], ci, co, out,
-            Hk=Hk, Hv=Hv, dk=dk, dv=dv, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
-            decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"])
-            for ci, co in ((S["conv_state"], cb), (cb, S["conv_state"]))]
-        for i in range(warmup):
-            calls_[i & 1].launch()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(calls):
-            calls_[i & 1].launch()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / calls
         state_bytes = 2 * B * Hv * dv * dk * 4
-        gbps = state_bytes / (ms * 1e-3) / 1e9
-        res[f"{dk}x{dv}"] = dict(us_per_launch=ms * 1e3, state_GBps=gbps,
-                                 pct_hbm_peak=100 * gbps / HBM_PEAK_GBS)
-        del S, W, calls_
+        r = {}
+        for hint in (False, True):
+            calls_ = [ops.prepare_decode_layer(
+                x[:, :QK], x[:, QK:2 * QK], x[:, 2 * QK:], S["state"], S["conv_w"], ci, co, out,
+                Hk=Hk, Hv=Hv, dk=dk, dv=dv, head_map=synth.TILED, batch=B, a=S["a"], b=S["b"],
+                decay_param=S["A_log"], dt_bias=S["dt_bias"], z=S["z"], norm_weight=S["norm_w"],
+                stream_state=hint)
+                for ci, co in ((S["conv_state"], cb), (cb, S["conv_state"]))]
+            for i in range(warmup):
+                calls_[i & 1].launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(calls):
+                calls_[i & 1].launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / calls
+            gbps = state_bytes / (ms * 1e-3) / 1e9
+            sfx = "_hint" if hint else ""
+            r.update({f"us_per_launch{sfx}": ms * 1e3, f"state_GBps{sfx}": gbps,
+                      f"pct_hbm_peak{sfx}": 100 * gbps / HBM_PEAK_GBS})
+            del calls_
+        res[f"{dk}x{dv}"] = r
+        del S, W
     return dict(workload="fused decode layer per head shape (dk x dv): B=64 x 1 token, Hk=16, "
-                         "Hv=32, tiled map, bf16 N(0,1), fp32 state, back-to-back launches",
+                         "Hv=32, tiled map, bf16 N(0,1), fp32 state, back-to-back launches; "
+                         "*_hint: with GDN_STREAM_STATE",
                 **res)
 
 
@@ -382,7 +391,8 @@ PREFILL_OTHER_SHAPES = ((32, 32), (64, 64), (96, 96), (64, 128), (128, 64), (128
 
 
 def prefill_shapes_bench(torch, ops, synth, calls=10, warmup=2):
-    """The chunked prefill at the other built head shapes (the one-kernel f32 path):
+    """The chunked prefill at the other built head shapes (the f32 path: preparation
+    kernel per (chunk, k-head), carry per (sequence, v-head, 32 dv rows)):
     one sequence of T=4096 and the 8-sequence varlen batch, Hk=16, Hv=32, bf16
     N(0,1) inputs, raw gates, core output; tokens/s, and the state-and-activation
     bytes per call over the call time against 8 TB/s."""
