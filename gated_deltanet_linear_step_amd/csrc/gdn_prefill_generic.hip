@@ -566,23 +566,25 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
     // 16 or 48 mod 64 (Kn, Us).
     constexpr int PA = DK + 2, PK = DK + 16, PC = CC + 2, PU = kSlice + 16, PQ = kSlice + 4;
     constexpr int NSL = DV / kSlice;
-    // per thread: the words of one chunk's operands it moves into LDS
-    constexpr int WQK = CC * DK / NT, WU = CC * kSlice / NT, WA = CC * CC / NT;
+    // per thread: the 16-byte pieces of one chunk's operands it moves into LDS
+    // (the q / diag(e)k / W tiles split evenly; U's slice and Aqk may leave
+    // whole waves idle)
+    constexpr int NQ4 = CC * DK / 4, NU4 = CC * kSlice / 4, NA4 = CC * CC / 4;
+    constexpr int WQK = NQ4 / NT, WU = (NU4 + NT - 1) / NT, WA = (NA4 + NT - 1) / NT;
     // Q S^T and W S^T: NT1 tiles of 16 x 16; with fewer tiles than waves the
     // contraction over dk is split KS ways and the parts summed through LDS
     constexpr int NT1 = (CC / 16) * (kSlice / 16), KS = NW / NT1;
     // the output and the state update: NO + NU tiles, all contracting over the chunk
     constexpr int NO = (CC / 16) * (kSlice / 16), NU = (kSlice / 16) * (DK / 16);
-    static_assert(CC * DK % NT == 0 && CC * kSlice % NT == 0 && CC * CC % NT == 0 && 3 * CC <= NT,
-                  "operand split");
+    static_assert(NQ4 % NT == 0 && NU4 % 64 == 0 && NA4 % 64 == 0 && 3 * CC <= NT, "operand split");
     static_assert(NT1 <= NW && NW % NT1 == 0 && (DK / KS) % 8 == 0, "phase-1 tiles");
 
-    __shared__ float Ss[kSlice][PA];  // the state slice S[dv0 + j][i]
-    __shared__ float Qn[CC][PA];      // normalised q rows
-    __shared__ float Wm[CC][PA];      // W
-    __shared__ float Kn[CC][PK];      // exp(G_last - G_t) k_t
-    __shared__ float Us[CC][PU];      // U of the slice, then D = U - W S^T
-    __shared__ float Aq[CC][PC];      // scale * Aqk
+    __shared__ __attribute__((aligned(16))) float Ss[kSlice][PA];  // the state slice S[dv0 + j][i]
+    __shared__ __attribute__((aligned(16))) float Qn[CC][PA];      // normalised q rows
+    __shared__ __attribute__((aligned(16))) float Wm[CC][PA];      // W
+    __shared__ __attribute__((aligned(16))) float Kn[CC][PK];      // exp(G_last - G_t) k_t
+    __shared__ __attribute__((aligned(16))) float Us[CC][PU];      // U of the slice, then D = U - W S^T
+    __shared__ __attribute__((aligned(16))) float Aq[CC][PC];      // scale * Aqk
     __shared__ float Qs[CC][PQ];      // scale gamma_t (Q S^T)_t
     __shared__ float Dc[3][CC];       // scale gamma_t, exp(G_last - G_t), gamma_t
     __shared__ float Pq[KS > 1 ? KS - 1 : 1][KS > 1 ? CC : 1][PQ];  // split-k parts
@@ -619,14 +621,18 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
     for (int e = tid; e < kSlice * DK; e += NT)
         Ss[e / DK][e % DK] = Sg[e];
 
-    // the operands of one chunk, as registers: element tid + NT i of each array
-    float rq[WQK], rk[WQK], rw[WQK], ru[WU], ra[WA], rd;
+    // the operands of one chunk, as registers: 16-byte piece tid + NT i of each
+    // array (pieces past an array's end, whole waves, load nothing)
+    float4 rq[WQK], rk[WQK], rw[WQK], ru[WU], ra[WA];
+    float rd;
     auto fetch = [&](int ci) {
         const int64_t c = cfirst + ci;
-        const float *gq = p.gq + (c * Hk + kh) * CC * DK, *gk = p.gke + (c * Hv + h) * CC * DK;
-        const float *gw = p.gw + (c * Hv + h) * CC * DK;
+        const float4 *gq = reinterpret_cast<const float4 *>(p.gq + (c * Hk + kh) * CC * DK);
+        const float4 *gk = reinterpret_cast<const float4 *>(p.gke + (c * Hv + h) * CC * DK);
+        const float4 *gw = reinterpret_cast<const float4 *>(p.gw + (c * Hv + h) * CC * DK);
         const float *gu = p.gu + (c * Hv + h) * CC * DV + dv0;
-        const float *ga = p.gaq + (c * Hv + h) * CC * CC, *gd = p.gdec + (c * Hv + h) * 3 * CC;
+        const float4 *ga = reinterpret_cast<const float4 *>(p.gaq + (c * Hv + h) * CC * CC);
+        const float *gd = p.gdec + (c * Hv + h) * 3 * CC;
 #pragma unroll
         for (int i = 0; i < WQK; ++i) {
             rq[i] = gq[tid + NT * i];
@@ -635,13 +641,29 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
         }
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
-            const int e = tid + NT * i;
-            ru[i] = gu[(e / kSlice) * DV + e % kSlice];
+            const int e4 = tid + NT * i;
+            if (e4 < NU4)
+                ru[i] = *reinterpret_cast<const float4 *>(gu + (e4 / (kSlice / 4)) * DV + 4 * (e4 % (kSlice / 4)));
         }
 #pragma unroll
-        for (int i = 0; i < WA; ++i)
-            ra[i] = ga[tid + NT * i];
+        for (int i = 0; i < WA; ++i) {
+            const int e4 = tid + NT * i;
+            if (e4 < NA4)
+                ra[i] = ga[e4];
+        }
         rd = gd[min(tid, 3 * CC - 1)];
+    };
+    // 16-byte piece e4 of a row-major array with `len` floats per row into LDS
+    // rows of `pitch` floats: one 16-byte store when the pitch keeps rows 16-byte
+    // aligned, else two 8-byte stores
+    auto put4 = [](float *base, int pitch, int len, int e4, float4 v) {
+        float *d = base + (4 * e4 / len) * pitch + (4 * e4) % len;
+        if (pitch % 4 == 0) {
+            *reinterpret_cast<float4 *>(d) = v;
+        } else {
+            *reinterpret_cast<float2 *>(d) = make_float2(v.x, v.y);
+            *reinterpret_cast<float2 *>(d + 2) = make_float2(v.z, v.w);
+        }
     };
     fetch(0);
 
@@ -651,20 +673,22 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
         __syncthreads();  // the previous chunk is done with every buffer
 #pragma unroll
         for (int i = 0; i < WQK; ++i) {
-            const int e = tid + NT * i;
-            Qn[e / DK][e % DK] = rq[i];
-            Kn[e / DK][e % DK] = rk[i];
-            Wm[e / DK][e % DK] = rw[i];
+            const int e4 = tid + NT * i;
+            put4(&Qn[0][0], PA, DK, e4, rq[i]);
+            put4(&Kn[0][0], PK, DK, e4, rk[i]);
+            put4(&Wm[0][0], PA, DK, e4, rw[i]);
         }
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
-            const int e = tid + NT * i;
-            Us[e / kSlice][e % kSlice] = ru[i];
+            const int e4 = tid + NT * i;
+            if (e4 < NU4)
+                put4(&Us[0][0], PU, kSlice, e4, ru[i]);
         }
 #pragma unroll
         for (int i = 0; i < WA; ++i) {
-            const int e = tid + NT * i;
-            Aq[e / CC][e % CC] = ra[i];
+            const int e4 = tid + NT * i;
+            if (e4 < NA4)
+                put4(&Aq[0][0], PC, CC, e4, ra[i]);
         }
         if (tid < 3 * CC)
             Dc[tid / CC][tid % CC] = rd;
