@@ -571,13 +571,12 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
     // whole waves idle)
     constexpr int NQ4 = CC * DK / 4, NU4 = CC * kSlice / 4, NA4 = CC * CC / 4;
     constexpr int WQK = NQ4 / NT, WU = (NU4 + NT - 1) / NT, WA = (NA4 + NT - 1) / NT;
-    // Q S^T and W S^T: NT1 tiles of 16 x 16; with fewer tiles than waves the
-    // contraction over dk is split KS ways and the parts summed through LDS
-    constexpr int NT1 = (CC / 16) * (kSlice / 16), KS = NW / NT1;
+    // Q S^T and W S^T: NT1 tiles of 16 x 16 each, a tile per wave or a product per wave
+    constexpr int NT1 = (CC / 16) * (kSlice / 16);
     // the output and the state update: NO + NU tiles, all contracting over the chunk
     constexpr int NO = (CC / 16) * (kSlice / 16), NU = (kSlice / 16) * (DK / 16);
     static_assert(NQ4 % NT == 0 && NU4 % 64 == 0 && NA4 % 64 == 0 && 3 * CC <= NT, "operand split");
-    static_assert(NT1 <= NW && NW % NT1 == 0 && (DK / KS) % 8 == 0, "phase-1 tiles");
+    static_assert(NT1 == NW || 2 * NT1 == NW, "phase-1 tiles");
 
     __shared__ __attribute__((aligned(16))) float Ss[kSlice][PA];  // the state slice S[dv0 + j][i]
     __shared__ __attribute__((aligned(16))) float Qn[CC][PA];      // normalised q rows
@@ -587,8 +586,6 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
     __shared__ __attribute__((aligned(16))) float Aq[CC][PC];      // scale * Aqk
     __shared__ float Qs[CC][PQ];      // scale gamma_t (Q S^T)_t
     __shared__ float Dc[3][CC];       // scale gamma_t, exp(G_last - G_t), gamma_t
-    __shared__ float Pq[KS > 1 ? KS - 1 : 1][KS > 1 ? CC : 1][PQ];  // split-k parts
-    __shared__ float Pw[KS > 1 ? KS - 1 : 1][KS > 1 ? CC : 1][PQ];
 
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv, Hk = hc.Hk, G = Hv / Hk;
@@ -696,41 +693,39 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
             fetch(ci + 1);  // the next chunk's operands, in flight from here
         __syncthreads();
 
-        // -- Q S^T and W S^T on the entering state, one read of S for both;
-        // Qs = scale gamma_t (Q S^T), Us = D = U - W S^T
-        {
-            const int tile = wave % NT1, part = wave / NT1;
-            const int m0 = (tile / (kSlice / 16)) * 16, n0 = (tile % (kSlice / 16)) * 16;
+        // -- Q S^T and W S^T on the entering state; Qs = scale gamma_t (Q S^T), Us =
+        // D = U - W S^T. With a tile per wave, one read of S serves both products;
+        // with half as many tiles as waves (32-token chunks), each wave takes one
+        // product of one tile over the whole of dk.
+        if constexpr (NT1 == NW) {
+            const int m0 = (wave / (kSlice / 16)) * 16, n0 = (wave % (kSlice / 16)) * 16;
             f32x4 qa, wa;
-            mfma_tile2<DK / KS / 4>([&](int t, int i) { return Qn[t][i]; }, [&](int t, int i) { return Wm[t][i]; },
-                                    [&](int i, int j) { return Ss[j][i]; }, m0, n0, part * (DK / KS), qa, wa);
+            mfma_tile2<DK / 4>([&](int t, int i) { return Qn[t][i]; }, [&](int t, int i) { return Wm[t][i]; },
+                               [&](int i, int j) { return Ss[j][i]; }, m0, n0, 0, qa, wa);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = m0 + 4 * lg + r, j = n0 + li;
-                if (part == 0) {
-                    Qs[t][j] = Dc[0][t] * qa[r];
-                    Us[t][j] -= wa[r];
-                } else {
-                    Pq[part - 1][t][j] = qa[r];
-                    Pw[part - 1][t][j] = wa[r];
-                }
+                Qs[t][j] = Dc[0][t] * qa[r];
+                Us[t][j] -= wa[r];
+            }
+        } else {
+            const int tile = wave % NT1;
+            const int m0 = (tile / (kSlice / 16)) * 16, n0 = (tile % (kSlice / 16)) * 16;
+            if (wave < NT1) {
+                const f32x4 qa = mfma_tile<DK / 4>([&](int t, int i) { return Qn[t][i]; },
+                                                   [&](int i, int j) { return Ss[j][i]; }, m0, n0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Qs[m0 + 4 * lg + r][n0 + li] = Dc[0][m0 + 4 * lg + r] * qa[r];
+            } else {
+                const f32x4 wa = mfma_tile<DK / 4>([&](int t, int i) { return Wm[t][i]; },
+                                                   [&](int i, int j) { return Ss[j][i]; }, m0, n0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Us[m0 + 4 * lg + r][n0 + li] -= wa[r];
             }
         }
         __syncthreads();
-        if (KS > 1) {  // add the other parts of the split contraction
-            for (int e = tid; e < CC * kSlice; e += NT) {
-                const int t = e / kSlice, j = e % kSlice;
-                float sq = 0.f, sw = 0.f;
-#pragma unroll
-                for (int q = 0; q < KS - 1; ++q) {
-                    sq += Pq[q][t][j];
-                    sw += Pw[q][t][j];
-                }
-                Qs[t][j] = fmaf(Dc[0][t], sq, Qs[t][j]);
-                Us[t][j] -= sw;
-            }
-            __syncthreads();
-        }
 
         // -- the state update S <- gamma_last S + D^T diag(e) K and the output
         // O = Qs + (scale Aqk) D, as one list of tiles: the update's first, then the
