@@ -174,7 +174,7 @@ __device__ __forceinline__ f32x4 mfma_tile_lower(FA a, FB b, int m0, int n0)
 // ---------------------------------------------------------------- workspace
 
 struct GenWs {
-    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, q, ke, w, u, aq, dec, onorm, total;
+    size_t chunk_seq, chunk_start, chunk_len, seq_chunk0, seq_order, q, ke, w, u, aq, dec, onorm, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -196,6 +196,7 @@ GenWs gen_layout(int Hk, int Hv, int dk, int dv, int64_t MC, int N, int64_t tota
     L.chunk_start = take(sizeof(int32_t) * MC);
     L.chunk_len = take(sizeof(int32_t) * MC);
     L.seq_chunk0 = take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    L.seq_order = take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
     L.q = take(sizeof(float) * MC * Hk * C * dk);
     L.ke = take(sizeof(float) * MC * Hv * C * dk);
     L.w = take(sizeof(float) * MC * Hv * C * dk);
@@ -255,6 +256,22 @@ __global__ __launch_bounds__(256) void plan_generic_kernel(PrefillParams p)
         if (threadIdx.x == 255)
             base_s += scan[255];
         __syncthreads();
+    }
+    // The carry takes sequences longest first: its workgroups are sequential
+    // chains as long as their sequence, so the long ones start first and the
+    // short ones fill in behind. Up to 1024 sequences are ranked by length (ties
+    // by index); more keep their order.
+    for (int i = threadIdx.x; i < p.N; i += 256) {
+        int rank = i;
+        if (p.N <= 1024) {
+            const int li = p.cu[i + 1] - p.cu[i];
+            rank = 0;
+            for (int j = 0; j < p.N; ++j) {
+                const int lj = p.cu[j + 1] - p.cu[j];
+                rank += lj > li || (lj == li && j < i);
+            }
+        }
+        p.seq_order[rank] = i;
     }
 }
 
@@ -588,18 +605,11 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
     __shared__ float Dc[3][CC];       // scale gamma_t, exp(G_last - G_t), gamma_t
 
     const HeadCfg &hc = p.hc;
-    const int Hv = hc.Hv, Hk = hc.Hk, G = Hv / Hk;
-    // Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the 8 XCDs
-    // in turn). Each XCD takes a contiguous range of (sequence, k-head, v-head of
-    // that k-head, slice), so the slices of one v-head, and the v-heads of one
-    // k-head, read the chunk's q, k and W through the same L2.
-    const int nwg = (int)gridDim.x;
-    const int L = nwg % 8 == 0 ? (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int slice = L % NSL;
-    const int jv = (L / NSL) % G;
-    const int kh = (L / (NSL * G)) % Hk;
-    const int seq = L / (NSL * Hv);
-    const int h = hc.head_map == 0 ? kh * G + jv : kh + jv * Hk;
+    const int Hv = hc.Hv, Hk = hc.Hk;
+    const int slice = blockIdx.x % NSL;
+    const int h = (blockIdx.x / NSL) % Hv;
+    const int kh = k_head_of(hc.head_map, h, Hk, Hv);
+    const int seq = p.N == 1 ? 0 : p.seq_order[blockIdx.x / (NSL * Hv)];  // longest first
     const int dv0 = slice * kSlice;
     const bool one_seq = p.N == 1;
     const int start = one_seq ? 0 : p.cu[seq];
@@ -835,6 +845,7 @@ void prefill_generic_carve(PrefillParams &p, void *ws, int64_t max_chunks)
     p.chunk_start = reinterpret_cast<int32_t *>(b + L.chunk_start);
     p.chunk_len = reinterpret_cast<int32_t *>(b + L.chunk_len);
     p.seq_chunk0 = reinterpret_cast<int32_t *>(b + L.seq_chunk0);
+    p.seq_order = reinterpret_cast<int32_t *>(b + L.seq_order);
     p.gq = reinterpret_cast<float *>(b + L.q);
     p.gke = reinterpret_cast<float *>(b + L.ke);
     p.gw = reinterpret_cast<float *>(b + L.w);
