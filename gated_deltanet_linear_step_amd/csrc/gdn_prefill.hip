@@ -54,6 +54,14 @@ constexpr int C = kChunk;     // 64 tokens per chunk
 constexpr int DH = 128;       // head dim (dk = dv) of the built prefill
 constexpr int KP = DH + 8;    // padded f16 row (272 B): conflict-free 16-B MFMA operand reads
 constexpr int TP = C + 8;     // padded f16 row of a transposed [dim][token] tile (144 B)
+
+// Half offset of 16-byte block u (8 token slots) in row `row` of a transposed
+// tile: the blocks are XOR-swizzled by row / 8. LDS serves 16-byte accesses
+// eight lanes at a time over 32 banks. The pitch alone spreads the MFMA operand
+// reads (eight consecutive rows, one block); the swizzle spreads the transposing
+// stores (rows 4 dq + d for eight dq, one block), which the 144-byte pitch
+// alone maps onto two bank groups.
+__device__ __forceinline__ int tcol(int row, int u) { return 8 * (u ^ ((row >> 3) & 7)); }
 constexpr int AP = C + 4;     // padded f32 row of the 64x64 A / T matrix
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
         const int dk0 = perm_idx(4 * dq);  // slots 4dq .. 4dq+3 hold dk0 .. dk0+3
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            *reinterpret_cast<half8 *>(&KT[4 * dq + d][8 * oc]) = kt[d];
+            *reinterpret_cast<half8 *>(&KT[4 * dq + d][tcol(4 * dq + d, oc)]) = kt[d];
             *reinterpret_cast<half8 *>(kdst + (dk0 + d) * C + 8 * oc) = kt[d];
         }
     }
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
             }
 #pragma unroll
             for (int d = 0; d < 4; ++d)
-                *reinterpret_cast<half8 *>(&VT[4 * dq + d][8 * oc]) = vb[d];
+                *reinterpret_cast<half8 *>(&VT[4 * dq + d][tcol(4 * dq + d, oc)]) = vb[d];
         }
         if (j + 1 < G)
             load_v(vr, vhead(j + 1));  // the next v-head's rows, in flight from here
@@ -534,8 +542,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrefillParams p)
                 f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    u = mfma16(tu[ks], lds_half8(&VT[nt * 16 + li][ks * 32 + lg * 8]), u);
-                    w = mfma16(tw[ks], lds_half8(&KT[nt * 16 + li][ks * 32 + lg * 8]), w);
+                    u = mfma16(tu[ks], lds_half8(&VT[nt * 16 + li][tcol(nt * 16 + li, 4 * ks + lg)]), u);
+                    w = mfma16(tw[ks], lds_half8(&KT[nt * 16 + li][tcol(nt * 16 + li, 4 * ks + lg)]), w);
                 }
                 // -U^T: this lane's four tokens are adjacent in row dv
                 *reinterpret_cast<f32x4 *>(ud + (nt * 16 + li) * C + wave * 16 + lg * 4) = -u;
