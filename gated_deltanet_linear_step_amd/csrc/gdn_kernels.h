@@ -113,6 +113,7 @@ bool prefill_supported(int dk, int dv);
 // The one-kernel f32 path (gdn_prefill_generic.hip) for the shapes other than 128 x 128.
 bool prefill_generic_supported(int dk, int dv);
 int prefill_generic_chunk(int dk);
+int prefill_generic_carry_threads();  // threads per carry workgroup of the f32 path
 size_t prefill_generic_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                        int64_t total_tokens, bool norm);
 void prefill_generic_carve(PrefillParams &p, void *ws, int64_t max_chunks);

@@ -1264,7 +1264,7 @@ PrefillPlan prefill_plan(int N, int Hk, int Hv, int dk, int dv, int64_t num_chun
         pl.carry_kind = 2;
         pl.slices_per_wg = 2;
         pl.carry_workgroups = (int)((int64_t)N * Hv * (dv / 32));
-        pl.carry_threads = 256;
+        pl.carry_threads = prefill_generic_carry_threads();
         pl.prep_workgroups = (int)(num_chunks * Hk);
         return pl;
     }

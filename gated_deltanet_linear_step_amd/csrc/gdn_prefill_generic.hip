@@ -830,6 +830,8 @@ bool prefill_generic_supported(int dk, int dv)
 
 int prefill_generic_chunk(int dk) { return dk >= 256 ? 32 : 64; }
 
+int prefill_generic_carry_threads() { return kCarryThreads; }
+
 size_t prefill_generic_workspace_bytes(int Hk, int Hv, int dk, int dv, int64_t max_chunks, int N,
                                        int64_t total_tokens, bool norm)
 {

@@ -307,7 +307,8 @@ typedef struct gdn_launch_info {
                                   T > 1), 2 one token per sequence */
     int32_t nontemporal;       /* decode: 1 when GDN_STREAM_STATE selects the hinted kernel */
     int32_t carry_kind;        /* prefill: 0 split carry (compute + output wave per dv
-                                  slice), 1 carry (one wave per slice) */
+                                  slice), 1 carry (one wave per slice); 2 the f32 carry
+                                  of the head shapes other than 128 x 128 */
     int32_t slices_per_workgroup; /* prefill: 16-row dv slices per carry workgroup */
     int32_t workgroups;        /* grid of the decode kernel, or of the prefill carry */
     int32_t threads;           /* threads per workgroup of that kernel */

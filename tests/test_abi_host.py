@@ -327,7 +327,7 @@ def test_prefill_other_head_shapes_take_the_one_kernel_path(dk, dv):
     i = ops.prefill_launch_info(lengths, Hk=2, Hv=4, dk=dk, dv=dv, compute_units=256)
     assert (i["carry_kind"], i["slices_per_workgroup"]) == (2, 2)
     assert i["prep_workgroups"] == chunks * 2
-    assert i["workgroups"] == len(lengths) * 4 * (dv // 32) and i["threads"] == 256
+    assert i["workgroups"] == len(lengths) * 4 * (dv // 32) and i["threads"] == 512
     # the workspace: per (chunk, k-head) q, per (chunk, v-head) diag(e) K, W, U,
     # Aqk and decay rows, f32; the gated norm adds its f32 core output
     d = dims(dk=dk, dv=dv)
