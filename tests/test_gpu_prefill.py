@@ -415,7 +415,7 @@ def test_prefill_bad_offsets_leave_state_untouched():
     assert torch.equal(st, before)
 
 
-# ------------------------------------------------------------------ other head shapes (one-kernel f32 path)
+# ------------------------------------------------------------------ other head shapes (the f32 path)
 
 OTHER_SHAPES = [(32, 32), (64, 64), (96, 96), (64, 128), (128, 64), (128, 256), (256, 128),
                 (256, 256)]
@@ -496,9 +496,10 @@ def test_other_head_shapes_negative_rate_and_unnormalised(dk, dv):
     assert maxabs(f64(st[0]), S) <= TOL_STATE and maxabs(f64(st_split[0]), S) <= TOL_STATE
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (256, 128)])
 def test_other_head_shapes_long_sequence(dk, dv):
-    """T = 2048 (32 chunks) at the config-3 statistics (bf16 N(0,1), zero state)."""
+    """T = 2048 (32 chunks; 64 of 32 tokens at dk = 256) at the config-3 statistics
+    (bf16 N(0,1), zero state)."""
     P = synth.prefill(seed=77, lengths=[2048], Hk=4, Hv=8, dk=dk, dv=dv, head_map=synth.GROUPED)
     out, st = run_prefill(P)
     torch.cuda.synchronize()
@@ -507,3 +508,25 @@ def test_other_head_shapes_long_sequence(dk, dv):
                          decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]),
                          nthreads=threads())
     assert maxabs(f64(out), y) <= TOL_OUT and maxabs(f64(st), S) <= TOL_STATE
+
+
+@pytest.mark.parametrize("n_seqs", [300, 1100])
+def test_other_head_shapes_many_short_sequences(n_seqs):
+    """Hundreds of short sequences (0-5 tokens, empty ones included) through the f32
+    path: the carry takes up to 1024 sequences longest first and more in their
+    packed order, the chunk table spans several plan passes; every head, output and
+    state against the oracle."""
+    rng = np.random.default_rng(n_seqs)
+    lengths = [int(x) for x in rng.integers(0, 6, size=n_seqs)]
+    P = synth.prefill(seed=80, lengths=lengths, Hk=1, Hv=2, dk=32, dv=32, head_map=synth.GROUPED,
+                      state_std=0.05)
+    out, st = run_prefill(P)
+    torch.cuda.synchronize()
+    y, S = oracle.packed(f64(P["q"]), f64(P["k"]), f64(P["v"]), f64(P["state"]), synth.GROUPED,
+                         P["cu_seqlens"], a=f64(P["a"]), b=f64(P["b"]),
+                         decay_param=f64(P["A_log"]), dt_bias=f64(P["dt_bias"]),
+                         nthreads=threads())
+    empty = [i for i, n in enumerate(lengths) if n == 0]
+    assert empty and torch.equal(st[empty].cpu(), P["state"][empty])
+    assert maxabs(f64(out), y) <= TOL_OUT
+    assert maxabs(f64(st), S) <= TOL_STATE
