@@ -27,10 +27,11 @@
 //     chunk's operands are loaded into registers while the current one runs.
 //  4. norm_generic_kernel -- the gated RMS norm of the f32 core output.
 // Chunks are 64 tokens, 32 when dk = 256 (the LDS then holds the 256-wide tiles).
-// LDS row pitches are chosen by how the MFMA operand reads index each array, so
-// that the 64 lanes of one read hit 64 different banks: an array whose row is
-// the lane's m or n index (lane % 16) takes a pitch of 4 or 36 mod 64, one whose
-// row is the contracted index (lane / 16) a pitch of 16 or 48 mod 64.
+// LDS row pitches are chosen by how the MFMA operand reads index each array. The
+// LDS serves a 32-bit read in two halves of 32 lanes over 32 banks, so an array
+// whose row is the lane's m or n index (lane % 16, column lane / 16) takes a
+// pitch of 2 mod 4 floats, and one whose row is the contracted index (lane / 16,
+// column lane % 16) a pitch of 16 mod 32: both spread each half over 32 banks.
 
 #include "gdn_device.h"
 #include "gdn_kernels.h"
@@ -287,6 +288,8 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
     constexpr int NT = kPrepThreads, NW = NT / 64, NB = CC / 16;
     // v columns staged in LDS per pass
     constexpr int VSL = (CC == 64 && DK >= 128) ? 64 : (DV < 128 ? DV : 128);
+    // pitches: PA, PC for rows read by m or n index, PB, PV by the contracted
+    // index; PG for K K^T and Q K^T, written by output tile and read row-wise
     constexpr int PA = DK + 2, PB = DK + 16, PC = CC + 2, PG = CC + 4, PV = VSL + 16;
     constexpr int PQB = PA > PB ? PA : PB;
     static_assert(DV % VSL == 0 && CC % 16 == 0 && DK % 16 == 0 && CC * CC % NT == 0 && CC * DK % NT == 0 &&
@@ -576,11 +579,10 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
 {
     constexpr int CC = gen_chunk<DK>();
     constexpr int NT = kCarryThreads, NW = NT / 64;
-    // Row pitches (floats) chosen by how the MFMA operand reads index each array,
-    // so that the 64 lanes of one read hit 64 different banks: arrays whose row is
-    // the lane's m or n index (lane % 16) take a pitch of 4 or 36 mod 64 (Ss, Qn,
-    // Wm, Aq, Qs); arrays whose row is the contracted index (lane / 16) a pitch of
-    // 16 or 48 mod 64 (Kn, Us).
+    // Row pitches (floats), by how the MFMA operand reads index each array (see
+    // the top of the file): 2 mod 4 for rows read by m or n index (Ss, Qn, Wm,
+    // Aq), 16 mod 32 for rows read by the contracted index (Kn, Us); Qs, written
+    // and read by output tile (rows 4 (lane / 16) + r), 4 mod 32.
     constexpr int PA = DK + 2, PK = DK + 16, PC = CC + 2, PU = kSlice + 16, PQ = kSlice + 4;
     constexpr int NSL = DV / kSlice;
     // per thread: the 16-byte pieces of one chunk's operands it moves into LDS
