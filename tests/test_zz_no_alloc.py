@@ -57,6 +57,21 @@ def test_noalloc_prefill_matches_the_workspace_entry_point_two_calls():
     assert np.any(np.abs(out.float().cpu().numpy()) > 1e-3)
 
 
+@pytest.mark.parametrize("dk,dv", [(32, 32), (256, 128)])
+def test_noalloc_prefill_other_head_shapes_two_calls(dk, dv):
+    """The f32 path (its own workspace layout, 32-token chunks at dk = 256): the
+    same two calls in a row, bit for bit against the workspace entry point."""
+    P1 = synth.prefill(seed=84, lengths=[150, 0, 97], Hk=2, Hv=4, dk=dk, dv=dv,
+                       head_map=synth.TILED, state_std=0.05, with_z=True)
+    o_ref, st_ref, out, st = both(P1, gated=True, out_dtype=torch.float32)
+    assert torch.equal(out, o_ref) and torch.equal(st, st_ref)
+    P2 = synth.prefill(seed=85, lengths=[45], Hk=2, Hv=4, dk=dk, dv=dv, head_map=synth.GROUPED,
+                       state_std=0.05)
+    o_ref, st_ref, out, st = both(P2, gated=False, out_dtype=torch.bfloat16)
+    assert torch.equal(out, o_ref) and torch.equal(st, st_ref)
+    assert np.any(np.abs(out.float().cpu().numpy()) > 1e-3)
+
+
 def test_noalloc_prefill_refuses_more_than_its_scratch():
     P = synth.prefill(seed=83, lengths=[4096], Hk=16, Hv=32, head_map=synth.GROUPED)
     need = ops.prefill_workspace_bytes(Hk=16, Hv=32, dk=128, dv=128, num_seqs=1, total_tokens=4096)
