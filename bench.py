@@ -520,7 +520,7 @@ def cpu_baseline(seconds):
 
     f = lambda t: t.double().numpy()  # noqa: E731
     nproc = os.cpu_count() or 1
-    threads = max(1, min(16, nproc))  # a one-GPU machine's share of the host is 16 cores
+    threads = max(1, min(16, nproc))  # a one-GPU host's share of the cores: 16
     res = dict(kind="oracle", cores=threads, nproc=nproc, cpu_model=cpu_model())
 
     # --- the headline decode step: B=64, one token, conv + core, state GB/s
