@@ -48,6 +48,28 @@ constexpr int gen_chunk()
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// x as a pair of bf16 (hi = x rounded to nearest even, lo = the rest rounded),
+// hi + lo = x to about 2^-16 relative; a product of two such pairs taken as
+// hi*hi + hi*lo + lo*hi on bf16 MFMA keeps that accuracy with f32 range.
+__device__ __forceinline__ void bf16_split(float x, uint16_t &hi, uint16_t &lo)
+{
+    const __bf16 h = (__bf16)x;
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)h));
+}
+
+// Element idx of a workspace array of n values stored as a [hi block][lo block]
+// pair of bf16 arrays (4 bytes per value, as f32).
+__device__ __forceinline__ void put_pair(float *base, int64_t n, int64_t idx, float x)
+{
+    uint16_t *b = reinterpret_cast<uint16_t *>(base);
+    uint16_t h, l;
+    bf16_split(x, h, l);
+    b[idx] = h;
+    b[n + idx] = l;
+}
 
 // One 16 x 16 tile of sum_k a(m, k) b(k, n) over k in [kb, kb + 4 KSTEPS) on
 // v_mfma_f32_16x16x4_f32, as two accumulator chains (alternate k-steps) added at
@@ -380,7 +402,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
                 if (c < DK) {
                     Kc[r][c] = kv[m] * ik;
                     Qc(r, c) = qv[m] * iq;
-                    gq[r * DK + c] = qv[m] * iq;
+                    put_pair(gq, CC * DK, r * DK + c, qv[m] * iq);
                 }
             }
         }
@@ -468,15 +490,19 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
                 const int e = tid + NT * i, t = e / CC, s2 = e % CC;
                 const float dg = s2 <= t ? expf(G_s[t] - G_s[s2]) : 0.f;
                 Am[t][s2] = s2 < t ? beta_s[t] * dg * Gm[t][s2] : 0.f;
-                aq[e] = s2 <= t ? hc.scale * dg * Qk[t][s2] : 0.f;
+                put_pair(aq, CC * CC, e, s2 <= t ? hc.scale * dg * Qk[t][s2] : 0.f);
             }
             float *ke = p.gke + ((int64_t)chunk * Hv + h) * CC * DK;
 #pragma unroll
             for (int i = 0; i < CC * DK / NT; ++i) {
                 const int e = tid + NT * i, t = e / DK, c = e % DK;
-                const float kv = Kc[t][c];
-                Kb(t, c) = bg_s[t] * kv;
-                ke[e] = e_s[t] * kv;
+                Kb(t, c) = bg_s[t] * Kc[t][c];
+            }
+            // (diag(e) K)^T, [dk][token]: consecutive threads take consecutive tokens
+#pragma unroll
+            for (int i = 0; i < CC * DK / NT; ++i) {
+                const int e = tid + NT * i, c = e / CC, t = e % CC;
+                put_pair(ke, CC * DK, e, e_s[t] * Kc[t][c]);
             }
         }
         __syncthreads();
@@ -554,7 +580,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
                                                           [&](int s2, int i) { return Kb(s2, i); }, m0, n0);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        wg[(m0 + 4 * lg + r) * DK + n0 + li] = acc[r];
+                        put_pair(wg, CC * DK, (m0 + 4 * lg + r) * DK + n0 + li, acc[r]);
                 } else {
                     const int v = u - NWT;
                     const int m0 = (NB - 1 - v / (VSL / 16)) * 16, n0 = (v % (VSL / 16)) * 16;
@@ -573,38 +599,96 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
 
 constexpr int kCarryThreads = 512;  // 8 waves, two per SIMD
 
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 consecutive bf16 of an LDS row
+__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// C[m][n] += sum_k A[m][k] B[n][k] over k in [0, 32 KB) for a 16 x 16 tile, both
+// operands bf16 hi/lo pairs in LDS rows with k contiguous (pitches PA, PB). Lane
+// (li, lg) feeds A[m0 + li][32 kb + 8 lg ..] and B[n0 + li][32 kb + 8 lg ..] and
+// receives C[m0 + 4 lg + r][n0 + li] in element r; hi*hi in one chain, hi*lo +
+// lo*hi in another.
+template <int KB, int PA, int PB>
+__device__ __forceinline__ f32x4 tile_pair(const uint16_t *ah, const uint16_t *al, const uint16_t *bh,
+                                           const uint16_t *bl, int m0, int n0, f32x4 c)
+{
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int ao = (m0 + li) * PA + 8 * lg, bo = (n0 + li) * PB + 8 * lg;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a1 = lds8(ah + ao + 32 * kb), a2 = lds8(al + ao + 32 * kb);
+        const bf16x8 b1 = lds8(bh + bo + 32 * kb), b2 = lds8(bl + bo + 32 * kb);
+        c = mfma_bf16(a1, b1, c);
+        x = mfma_bf16(a1, b2, x);
+        x = mfma_bf16(a2, b1, x);
+    }
+    return c + x;
+}
+
+// Two tiles that share B: A1 B and A2 B (one read of B for both).
+template <int KB, int PA, int PB>
+__device__ __forceinline__ void tile_pair2(const uint16_t *a1h, const uint16_t *a1l, const uint16_t *a2h,
+                                           const uint16_t *a2l, const uint16_t *bh, const uint16_t *bl, int m0,
+                                           int n0, f32x4 &r1, f32x4 &r2)
+{
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int ao = (m0 + li) * PA + 8 * lg, bo = (n0 + li) * PB + 8 * lg;
+    f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, x1 = c1, c2 = c1, x2 = c1;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 b1 = lds8(bh + bo + 32 * kb), b2 = lds8(bl + bo + 32 * kb);
+        const bf16x8 p1 = lds8(a1h + ao + 32 * kb), p2 = lds8(a1l + ao + 32 * kb);
+        const bf16x8 q1 = lds8(a2h + ao + 32 * kb), q2 = lds8(a2l + ao + 32 * kb);
+        c1 = mfma_bf16(p1, b1, c1);
+        c2 = mfma_bf16(q1, b1, c2);
+        x1 = mfma_bf16(p1, b2, x1);
+        x2 = mfma_bf16(q1, b2, x2);
+        x1 = mfma_bf16(p2, b1, x1);
+        x2 = mfma_bf16(q2, b1, x2);
+    }
+    r1 = c1 + x1;
+    r2 = c2 + x2;
+}
+
+// Per (sequence, v-head, 32 dv rows). The slice's state is held in f32 MFMA
+// accumulators for the whole call: each wave owns fixed 16 x 16 state tiles
+// (rows dv, columns dk), updates them in place every chunk and publishes them to
+// LDS as bf16 hi/lo for the next chunk's Q S^T and W S^T. Every product is three
+// bf16 MFMAs (hi*hi + hi*lo + lo*hi) on operands the preparation kernel stored as
+// hi/lo pairs.
 template <int DK, int DV>
 __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void carry_generic_kernel(
     PrefillParams p)
 {
     constexpr int CC = gen_chunk<DK>();
     constexpr int NT = kCarryThreads, NW = NT / 64;
-    // Row pitches (floats), by how the MFMA operand reads index each array (see
-    // the top of the file): 2 mod 4 for rows read by m or n index (Ss, Qn, Wm,
-    // Aq), 16 mod 32 for rows read by the contracted index (Kn, Us); Qs, written
-    // and read by output tile (rows 4 (lane / 16) + r), 4 mod 32.
-    constexpr int PA = DK + 2, PK = DK + 16, PC = CC + 2, PU = kSlice + 16, PQ = kSlice + 4;
     constexpr int NSL = DV / kSlice;
-    // per thread: the 16-byte pieces of one chunk's operands it moves into LDS
-    // (the q / diag(e)k / W tiles split evenly; U's slice and Aqk may leave
-    // whole waves idle)
-    constexpr int NQ4 = CC * DK / 4, NU4 = CC * kSlice / 4, NA4 = CC * CC / 4;
-    constexpr int WQK = NQ4 / NT, WU = (NU4 + NT - 1) / NT, WA = (NA4 + NT - 1) / NT;
-    // Q S^T and W S^T: NT1 tiles of 16 x 16 each, a tile per wave or a product per wave
-    constexpr int NT1 = (CC / 16) * (kSlice / 16);
-    // the output and the state update: NO + NU tiles, all contracting over the chunk
-    constexpr int NO = (CC / 16) * (kSlice / 16), NU = (kSlice / 16) * (DK / 16);
-    static_assert(NQ4 % NT == 0 && NU4 % 64 == 0 && NA4 % 64 == 0 && 3 * CC <= NT, "operand split");
+    // bf16 row pitches: rows 16-byte aligned, and 8 consecutive rows start in 8
+    // different 16-byte bank groups (the 16-byte operand reads take 8 lanes a pass)
+    constexpr int PK = DK + 8, PC = CC + 8;
+    constexpr int NT1 = (CC / 16) * (kSlice / 16);  // Q S^T / W S^T tiles = output tiles
+    constexpr int NU = (kSlice / 16) * (DK / 16);   // state tiles
+    constexpr int NUW = (NU + NW - 1) / NW;         // state tiles per wave
+    constexpr int KB = DK / 32, CB = CC / 32;       // 32-wide k blocks over dk, over the chunk
+    // 16-byte pieces of one chunk's operands (hi and lo halves): q, W and
+    // (diag(e) K)^T split evenly over the threads, Aqk may leave whole waves idle
+    constexpr int NQ = 2 * CC * DK / 8, NA = 2 * CC * CC / 8;
+    constexpr int WQ = NQ / NT, WA = (NA + NT - 1) / NT;
     static_assert(NT1 == NW || 2 * NT1 == NW, "phase-1 tiles");
+    static_assert(NQ % NT == 0 && NA % 64 == 0 && DK % 32 == 0 && CC % 32 == 0 && 3 * CC <= NT, "shape");
 
-    __shared__ __attribute__((aligned(16))) float Ss[kSlice][PA];  // the state slice S[dv0 + j][i]
-    __shared__ __attribute__((aligned(16))) float Qn[CC][PA];      // normalised q rows
-    __shared__ __attribute__((aligned(16))) float Wm[CC][PA];      // W
-    __shared__ __attribute__((aligned(16))) float Kn[CC][PK];      // exp(G_last - G_t) k_t
-    __shared__ __attribute__((aligned(16))) float Us[CC][PU];      // U of the slice, then D = U - W S^T
-    __shared__ __attribute__((aligned(16))) float Aq[CC][PC];      // scale * Aqk
-    __shared__ float Qs[CC][PQ];      // scale gamma_t (Q S^T)_t
-    __shared__ float Dc[3][CC];       // scale gamma_t, exp(G_last - G_t), gamma_t
+    __shared__ __attribute__((aligned(16))) uint16_t Sh[kSlice][PK], Sl[kSlice][PK];  // S[j][i], hi / lo
+    __shared__ __attribute__((aligned(16))) uint16_t Qh[CC][PK], Ql[CC][PK];          // normalised q rows
+    __shared__ __attribute__((aligned(16))) uint16_t Wh[CC][PK], Wl[CC][PK];          // W rows
+    __shared__ __attribute__((aligned(16))) uint16_t Kh[DK][PC], Kl[DK][PC];          // (diag(e) K)^T
+    __shared__ __attribute__((aligned(16))) uint16_t Dh[kSlice][PC], Dl[kSlice][PC];  // D^T of the slice
+    __shared__ __attribute__((aligned(16))) uint16_t Ah[CC][PC], Al[CC][PC];          // scale * Aqk
+    __shared__ float Dc[3][CC];  // scale gamma_t, exp(G_last - G_t), gamma_t
 
     const HeadCfg &hc = p.hc;
     const int Hv = hc.Hv, Hk = hc.Hk;
@@ -627,150 +711,167 @@ __global__ __launch_bounds__(kCarryThreads, 1) __attribute__((amdgpu_waves_per_e
     void *obase = (flags & F_GATED_NORM) ? static_cast<void *>(p.onorm) : p.out;
     const int odt = (flags & F_GATED_NORM) ? DT_F32 : p.out_dt;
 
-    for (int e = tid; e < kSlice * DK; e += NT)
-        Ss[e / DK][e % DK] = Sg[e];
+    // phase-1 tile of this wave: rows m1 (tokens), columns n1 (dv). With a tile per
+    // wave the wave forms Q S^T and D; with two waves per tile (32-token chunks)
+    // the first forms Q S^T, the second D. The Q S^T wave also owns the output tile.
+    const int t1 = NT1 == NW ? wave : wave % NT1;
+    const int m1 = (t1 / (kSlice / 16)) * 16, n1 = (t1 % (kSlice / 16)) * 16;
+    const bool makes_q = NT1 == NW || wave < NT1, makes_d = NT1 == NW || wave >= NT1;
 
-    // the operands of one chunk, as registers: 16-byte piece tid + NT i of each
-    // array (pieces past an array's end, whole waves, load nothing)
-    float4 rq[WQK], rk[WQK], rw[WQK], ru[WU], ra[WA];
-    float rd;
+    // the state tiles this wave owns: tile u = wave + NW k, rows (dv) 16 (u % 2),
+    // columns (dk) 16 (u / 2)
+    f32x4 S[NUW];
+    auto publish = [&](int k, int u) {  // the tile's bf16 hi / lo for the next Q S^T, W S^T
+        const int m0 = (u % 2) * 16, n0 = (u / 2) * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            bf16_split(S[k][r], Sh[m0 + 4 * lg + r][n0 + li], Sl[m0 + 4 * lg + r][n0 + li]);
+    };
+#pragma unroll
+    for (int k = 0; k < NUW; ++k) {
+        const int u = wave + NW * k;
+        if (u < NU) {
+            const int m0 = (u % 2) * 16, n0 = (u / 2) * 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[k][r] = Sg[(m0 + 4 * lg + r) * DK + n0 + li];
+            publish(k, u);
+        }
+    }
+
+    // one chunk's operands in registers: 16-byte piece tid + NT i of each array;
+    // U at this wave's phase-1 tile positions (the D wave only)
+    uint4 rq[WQ], rw[WQ], rk[WQ], ra[WA];
+    float ru[4] = {0.f, 0.f, 0.f, 0.f}, rd;
     auto fetch = [&](int ci) {
         const int64_t c = cfirst + ci;
-        const float4 *gq = reinterpret_cast<const float4 *>(p.gq + (c * Hk + kh) * CC * DK);
-        const float4 *gk = reinterpret_cast<const float4 *>(p.gke + (c * Hv + h) * CC * DK);
-        const float4 *gw = reinterpret_cast<const float4 *>(p.gw + (c * Hv + h) * CC * DK);
-        const float *gu = p.gu + (c * Hv + h) * CC * DV + dv0;
-        const float4 *ga = reinterpret_cast<const float4 *>(p.gaq + (c * Hv + h) * CC * CC);
-        const float *gd = p.gdec + (c * Hv + h) * 3 * CC;
+        const uint4 *gq = reinterpret_cast<const uint4 *>(p.gq + (c * Hk + kh) * CC * DK);
+        const uint4 *gk = reinterpret_cast<const uint4 *>(p.gke + (c * Hv + h) * CC * DK);
+        const uint4 *gw = reinterpret_cast<const uint4 *>(p.gw + (c * Hv + h) * CC * DK);
+        const uint4 *ga = reinterpret_cast<const uint4 *>(p.gaq + (c * Hv + h) * CC * CC);
 #pragma unroll
-        for (int i = 0; i < WQK; ++i) {
+        for (int i = 0; i < WQ; ++i) {
             rq[i] = gq[tid + NT * i];
-            rk[i] = gk[tid + NT * i];
             rw[i] = gw[tid + NT * i];
-        }
-#pragma unroll
-        for (int i = 0; i < WU; ++i) {
-            const int e4 = tid + NT * i;
-            if (e4 < NU4)
-                ru[i] = *reinterpret_cast<const float4 *>(gu + (e4 / (kSlice / 4)) * DV + 4 * (e4 % (kSlice / 4)));
+            rk[i] = gk[tid + NT * i];
         }
 #pragma unroll
         for (int i = 0; i < WA; ++i) {
-            const int e4 = tid + NT * i;
-            if (e4 < NA4)
-                ra[i] = ga[e4];
+            const int e = tid + NT * i;
+            if (e < NA)
+                ra[i] = ga[e];
         }
-        rd = gd[min(tid, 3 * CC - 1)];
+        if (makes_d) {
+            const float *gu = p.gu + (c * Hv + h) * CC * DV + dv0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ru[r] = gu[(m1 + 4 * lg + r) * DV + n1 + li];
+        }
+        rd = p.gdec[(c * Hv + h) * 3 * CC + min(tid, 3 * CC - 1)];
     };
-    // 16-byte piece e4 of a row-major array with `len` floats per row into LDS
-    // rows of `pitch` floats: one 16-byte store when the pitch keeps rows 16-byte
-    // aligned, else two 8-byte stores
-    auto put4 = [](float *base, int pitch, int len, int e4, float4 v) {
-        float *d = base + (4 * e4 / len) * pitch + (4 * e4) % len;
-        if (pitch % 4 == 0) {
-            *reinterpret_cast<float4 *>(d) = v;
-        } else {
-            *reinterpret_cast<float2 *>(d) = make_float2(v.x, v.y);
-            *reinterpret_cast<float2 *>(d + 2) = make_float2(v.z, v.w);
-        }
+    // piece e of a [hi block][lo block] pair of row-major arrays with `len` values a
+    // row (nh pieces a block) into LDS rows of `pitch` bf16; the hi/lo choice is
+    // uniform over a wave (nh is a multiple of 64)
+    auto put8 = [](uint16_t *hi, uint16_t *lo, int pitch, int len, int nh, int e, uint4 v) {
+        const bool second = e >= nh;
+        const int e2 = second ? e - nh : e;
+        *reinterpret_cast<uint4 *>((second ? lo : hi) + (8 * e2 / len) * pitch + (8 * e2) % len) = v;
     };
     fetch(0);
 
     for (int ci = 0; ci < nch; ++ci) {
         const int n = min(CC, len - ci * CC);
         const int64_t tok0 = start + (int64_t)ci * CC;
-        __syncthreads();  // the previous chunk is done with every buffer
+        __syncthreads();  // the previous chunk is done with every buffer; S published
 #pragma unroll
-        for (int i = 0; i < WQK; ++i) {
-            const int e4 = tid + NT * i;
-            put4(&Qn[0][0], PA, DK, e4, rq[i]);
-            put4(&Kn[0][0], PK, DK, e4, rk[i]);
-            put4(&Wm[0][0], PA, DK, e4, rw[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < WU; ++i) {
-            const int e4 = tid + NT * i;
-            if (e4 < NU4)
-                put4(&Us[0][0], PU, kSlice, e4, ru[i]);
+        for (int i = 0; i < WQ; ++i) {
+            const int e = tid + NT * i;
+            put8(&Qh[0][0], &Ql[0][0], PK, DK, NQ / 2, e, rq[i]);
+            put8(&Wh[0][0], &Wl[0][0], PK, DK, NQ / 2, e, rw[i]);
+            put8(&Kh[0][0], &Kl[0][0], PC, CC, NQ / 2, e, rk[i]);
         }
 #pragma unroll
         for (int i = 0; i < WA; ++i) {
-            const int e4 = tid + NT * i;
-            if (e4 < NA4)
-                put4(&Aq[0][0], PC, CC, e4, ra[i]);
+            const int e = tid + NT * i;
+            if (e < NA)
+                put8(&Ah[0][0], &Al[0][0], PC, CC, NA / 2, e, ra[i]);
         }
         if (tid < 3 * CC)
             Dc[tid / CC][tid % CC] = rd;
+        float uc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            uc[r] = ru[r];
         if (ci + 1 < nch)
             fetch(ci + 1);  // the next chunk's operands, in flight from here
         __syncthreads();
 
-        // -- Q S^T and W S^T on the entering state; Qs = scale gamma_t (Q S^T), Us =
-        // D = U - W S^T. With a tile per wave, one read of S serves both products;
-        // with half as many tiles as waves (32-token chunks), each wave takes one
-        // product of one tile over the whole of dk.
+        // -- Q S^T and D = U - W S^T on the entering state; this wave keeps
+        // scale gamma_t (Q S^T) of its output tile in registers and publishes D^T
+        f32x4 qv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
         if constexpr (NT1 == NW) {
-            const int m0 = (wave / (kSlice / 16)) * 16, n0 = (wave % (kSlice / 16)) * 16;
-            f32x4 qa, wa;
-            mfma_tile2<DK / 4>([&](int t, int i) { return Qn[t][i]; }, [&](int t, int i) { return Wm[t][i]; },
-                               [&](int i, int j) { return Ss[j][i]; }, m0, n0, 0, qa, wa);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = m0 + 4 * lg + r, j = n0 + li;
-                Qs[t][j] = Dc[0][t] * qa[r];
-                Us[t][j] -= wa[r];
-            }
+            tile_pair2<KB, PK, PK>(&Qh[0][0], &Ql[0][0], &Wh[0][0], &Wl[0][0], &Sh[0][0], &Sl[0][0], m1, n1, qv, wv);
+        } else if (makes_q) {
+            qv = tile_pair<KB, PK, PK>(&Qh[0][0], &Ql[0][0], &Sh[0][0], &Sl[0][0], m1, n1, qv);
         } else {
-            const int tile = wave % NT1;
-            const int m0 = (tile / (kSlice / 16)) * 16, n0 = (tile % (kSlice / 16)) * 16;
-            if (wave < NT1) {
-                const f32x4 qa = mfma_tile<DK / 4>([&](int t, int i) { return Qn[t][i]; },
-                                                   [&](int i, int j) { return Ss[j][i]; }, m0, n0);
+            wv = tile_pair<KB, PK, PK>(&Wh[0][0], &Wl[0][0], &Sh[0][0], &Sl[0][0], m1, n1, wv);
+        }
+        if (makes_q) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Qs[m0 + 4 * lg + r][n0 + li] = Dc[0][m0 + 4 * lg + r] * qa[r];
-            } else {
-                const f32x4 wa = mfma_tile<DK / 4>([&](int t, int i) { return Wm[t][i]; },
-                                                   [&](int i, int j) { return Ss[j][i]; }, m0, n0);
+            for (int r = 0; r < 4; ++r)
+                qv[r] *= Dc[0][m1 + 4 * lg + r];
+        }
+        if (makes_d) {  // D^T[j][t]: this lane's 4 consecutive tokens of row j
+            uint16_t dh[4], dl[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Us[m0 + 4 * lg + r][n0 + li] -= wa[r];
-            }
+            for (int r = 0; r < 4; ++r)
+                bf16_split(uc[r] - wv[r], dh[r], dl[r]);
+            *reinterpret_cast<uint2 *>(&Dh[n1 + li][m1 + 4 * lg]) =
+                make_uint2(dh[0] | ((uint32_t)dh[1] << 16), dh[2] | ((uint32_t)dh[3] << 16));
+            *reinterpret_cast<uint2 *>(&Dl[n1 + li][m1 + 4 * lg]) =
+                make_uint2(dl[0] | ((uint32_t)dl[1] << 16), dl[2] | ((uint32_t)dl[3] << 16));
         }
         __syncthreads();
 
-        // -- the state update S <- gamma_last S + D^T diag(e) K and the output
-        // O = Qs + (scale Aqk) D, as one list of tiles: the update's first, then the
-        // output's from the longest contraction down (Aqk is zero above the
-        // diagonal, so output rows m0 .. m0 + 15 contract over the first m0 + 16)
+        // -- the state update S <- gamma_last S + D^T (diag(e) K) on this wave's
+        // tiles (contracting over the chunk's tokens), published for the next chunk
         const float gl = Dc[2][CC - 1];
-        for (int u = wave; u < NU + NO; u += NW) {
+#pragma unroll
+        for (int k = 0; k < NUW; ++k) {
+            const int u = wave + NW * k;
             if (u < NU) {
-                const int m0 = (u % (kSlice / 16)) * 16, n0 = (u / (kSlice / 16)) * 16;
-                const f32x4 acc = mfma_tile<CC / 4>([&](int j, int t) { return Us[t][j]; },
-                                                    [&](int t, int i) { return Kn[t][i]; }, m0, n0);
+                S[k] = tile_pair<CB, PC, PC>(&Dh[0][0], &Dl[0][0], &Kh[0][0], &Kl[0][0], (u % 2) * 16,
+                                             (u / 2) * 16, S[k] * gl);
+                publish(k, u);
+            }
+        }
+        // -- the output tile: O = scale gamma (Q S^T) + (scale Aqk) D, contracting
+        // only over the 32-token blocks at or below the tile's last row (Aqk is
+        // zero above the diagonal)
+        if (makes_q) {
+            f32x4 o = qv;
+            if (m1 < 32)
+                o = tile_pair<1, PC, PC>(&Ah[0][0], &Al[0][0], &Dh[0][0], &Dl[0][0], m1, n1, o);
+            else
+                o = tile_pair<CB, PC, PC>(&Ah[0][0], &Al[0][0], &Dh[0][0], &Dl[0][0], m1, n1, o);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = m0 + 4 * lg + r, i = n0 + li;
-                    Ss[j][i] = fmaf(gl, Ss[j][i], acc[r]);
-                }
-            } else {
-                const int o = u - NU;
-                const int m0 = (CC / 16 - 1 - o / (kSlice / 16)) * 16, n0 = (o % (kSlice / 16)) * 16;
-                const f32x4 acc = mfma_tile_lower<CC>([&](int t, int s) { return Aq[t][s]; },
-                                                      [&](int s, int j) { return Us[s][j]; }, m0, n0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = m0 + 4 * lg + r, j = n0 + li;
-                    if (t < n)
-                        store_act(obase, ((tok0 + t) * Hv + h) * DV + dv0 + j, odt, Qs[t][j] + acc[r]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = m1 + 4 * lg + r;
+                if (t < n)
+                    store_act(obase, ((tok0 + t) * Hv + h) * DV + dv0 + n1 + li, odt, o[r]);
             }
         }
     }
-    __syncthreads();
-    for (int e = tid; e < kSlice * DK; e += NT)
-        Sg[e] = Ss[e / DK][e % DK];
+#pragma unroll
+    for (int k = 0; k < NUW; ++k) {
+        const int u = wave + NW * k;
+        if (u < NU) {
+            const int m0 = (u % 2) * 16, n0 = (u / 2) * 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sg[(m0 + 4 * lg + r) * DK + n0 + li] = S[k][r];
+        }
+    }
 }
 
 // ---------------------------------------------------------------- 4. gated norm
