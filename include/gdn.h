@@ -244,8 +244,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_seqs, int32
  * sequences). Each path runs a kernel parallel over (chunk, k-head) that forms
  * the chunk's own quantities, then a carry per (sequence, v-head, slice of dv
  * rows) that runs the state-dependent products chunk after chunk. dk = dv = 128
- * takes f16 MFMA operands; the other head shapes compute in f32 throughout, on
- * f32 MFMA, and their workspace is f32. The result equals
+ * takes f16 MFMA operands; the other head shapes keep f32 accuracy (f32 MFMA,
+ * and bf16 hi/lo operand pairs on bf16 MFMA in the carry). The result equals
  * the token-by-token recurrence up to rounding order (ferrox-core src/gdn.rs
  * module doc: the chunked form is the same recurrence summed in another order;
  * ferrum-kernels tests page, `chunked_c64_matches_recurrent_oracle_and_
