@@ -82,9 +82,11 @@ struct PrefillParams {
     uint16_t *aqk;         // [num_chunks][Hv][64][64]   f16, -scale (masked decayed Q K^T)
     float *gcum;           // [num_chunks][Hv][4][64]    f32, exp(G_t), -exp(G_last - G_t), scale exp(G_t), 0
     float *onorm;          // [total][Hv][dv]            f32 core output (gated norm only)
-    // the f32 path of the other head shapes (C = its chunk length), all f32
+    // the f32-accuracy path of the other head shapes (C = its chunk length): gq,
+    // gke, gw and gaq hold per (chunk, head) a bf16 hi block then a bf16 lo block
+    // (4 bytes a value); gu and gdec are f32
     float *gq;             // [num_chunks][Hk][C][dk]    normalised q rows
-    float *gke;            // [num_chunks][Hv][C][dk]    exp(G_last - G_t) k_t (normalised k)
+    float *gke;            // [num_chunks][Hv][dk][C]    (diag(exp(G_last - G_t)) K)^T (normalised k)
     float *gw;             // [num_chunks][Hv][C][dk]    W = T diag(beta gamma) K
     float *gu;             // [num_chunks][Hv][C][dv]    U = T diag(beta) V
     float *gaq;            // [num_chunks][Hv][C][C]     scale * (masked decayed Q K^T)

@@ -12,7 +12,9 @@
 //     O   = scale (diag(gamma) Q S^T + Aqk D),  Aqk = lower-incl(exp(G_t - G_s) q_t . k_s)
 //     S  <- gamma_last S + D^T diag(exp(G_last - G_t)) K
 //
-// Kernels (all arithmetic f32; every product on v_mfma_f32_16x16x4_f32):
+// Kernels (f32 accuracy throughout: the preparation's products on
+// v_mfma_f32_16x16x4_f32, the carry's on v_mfma_f32_16x16x32_bf16 with each f32
+// operand split into a bf16 hi/lo pair):
 //  1. plan_generic_kernel -- the chunk table (several sequences only; one
 //     sequence's chunk bounds are closed-form).
 //  2. prep_generic_kernel -- per (chunk, k-head), all chunks in parallel: the
@@ -22,9 +24,10 @@
 //     by block products), W, U, scale * Aqk, diag(e) K and the decay rows, all to
 //     the workspace.
 //  3. carry_generic_kernel -- per (sequence, v-head, 32 rows of dv), sequential
-//     over the sequence's chunks with the slice's f32 state resident in LDS: only
-//     the state-dependent products (Q S^T, W S^T, Aqk D, D^T diag(e) K). The next
-//     chunk's operands are loaded into registers while the current one runs.
+//     over the sequence's chunks with the slice's f32 state resident in MFMA
+//     accumulators: only the state-dependent products (Q S^T, W S^T, Aqk D,
+//     D^T diag(e) K). The next chunk's operands are loaded into registers while
+//     the current one runs.
 //  4. norm_generic_kernel -- the gated RMS norm of the f32 core output.
 // Chunks are 64 tokens, 32 when dk = 256 (the LDS then holds the 256-wide tiles).
 // LDS row pitches are chosen by how the MFMA operand reads index each array. The
@@ -203,8 +206,9 @@ struct GenWs {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // MC = the chunk count bound (total / chunk + N); per (chunk, k-head) the
-// normalised q rows, per (chunk, v-head) diag(e) K, W, U, scale * Aqk and three
-// decay rows, all f32; with the gated norm an f32 core output.
+// normalised q rows, per (chunk, v-head) (diag(e) K)^T, W and scale * Aqk, each
+// as a [hi block][lo block] pair of bf16 arrays (4 bytes a value), and U and
+// three decay rows in f32; with the gated norm an f32 core output.
 GenWs gen_layout(int Hk, int Hv, int dk, int dv, int64_t MC, int N, int64_t total, bool norm)
 {
     const int C = dk >= 256 ? 32 : 64;
