@@ -104,15 +104,15 @@ DecodePlan decode_plan(int dk, int dv, int B, int T, int Hv, bool fused_conv, ui
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
 // Which carry kernel a prefill runs: kind 0 = carry_split (compute and output waves
-// per slice), 1 = carry (one wave per slice), 2 = the one-kernel f32 path of the
-// other head shapes (no prep kernel); dv slices of 16 rows per workgroup;
+// per slice), 1 = carry (one wave per slice), 2 = the carry of the f32-accuracy
+// path of the other head shapes (32 dv rows per workgroup); dv slices of 16 rows per workgroup;
 // carry workgroups and threads per workgroup; prep workgroups. launch_prefill
 // launches exactly this for the device's compute-unit count.
 struct PrefillPlan {
     int carry_kind, slices_per_wg, carry_workgroups, carry_threads, prep_workgroups;
 };
 bool prefill_supported(int dk, int dv);
-// The one-kernel f32 path (gdn_prefill_generic.hip) for the shapes other than 128 x 128.
+// The f32-accuracy path (gdn_prefill_generic.hip) for the shapes other than 128 x 128.
 bool prefill_generic_supported(int dk, int dv);
 int prefill_generic_chunk(int dk);
 int prefill_generic_carry_threads();  // threads per carry workgroup of the f32 path
