@@ -1182,8 +1182,8 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillParams p)
 
 }  // namespace
 
-// 128 x 128 runs the MFMA kernels of this file; the decode's other head shapes
-// run the one-kernel f32 path of gdn_prefill_generic.hip.
+// 128 x 128 runs the f16-operand MFMA kernels of this file; the decode's other
+// head shapes run the f32-accuracy path of gdn_prefill_generic.hip.
 bool prefill_supported(int dk, int dv) { return (dk == DH && dv == DH) || prefill_generic_supported(dk, dv); }
 
 bool prefill_is_mfma(int dk, int dv) { return dk == DH && dv == DH; }
