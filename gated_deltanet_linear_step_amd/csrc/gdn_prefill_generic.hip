@@ -84,7 +84,7 @@ __device__ __forceinline__ f32x4 mfma_tile(FA a, FB b, int m0, int n0, int kb = 
     static_assert(KSTEPS % 2 == 0, "two chains");
     // operands are read a block of BLK k-steps at a time, the next block's reads
     // issued before this block's products
-    constexpr int BLK = KSTEPS < 16 ? KSTEPS : 16;
+    constexpr int BLK = KSTEPS % 8 == 0 ? 8 : KSTEPS;
     static_assert(KSTEPS % BLK == 0, "blocks");
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
@@ -314,9 +314,8 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
     constexpr int NT = kPrepThreads, NW = NT / 64, NB = CC / 16;
     // v columns staged in LDS per pass
     constexpr int VSL = (CC == 64 && DK >= 128) ? 64 : (DV < 128 ? DV : 128);
-    // pitches: PA, PC for rows read by m or n index, PB, PV by the contracted
-    // index; PG for K K^T and Q K^T, written by output tile and read row-wise
-    constexpr int PA = DK + 2, PB = DK + 16, PC = CC + 2, PG = CC + 4, PV = VSL + 16;
+    // pitches: PA, PC for rows read by m or n index, PB, PV by the contracted index
+    constexpr int PA = DK + 2, PB = DK + 16, PC = CC + 2, PV = VSL + 16;
     constexpr int PQB = PA > PB ? PA : PB;
     static_assert(DV % VSL == 0 && CC % 16 == 0 && DK % 16 == 0 && CC * CC % NT == 0 && CC * DK % NT == 0 &&
                       CC * VSL % NT == 0 && CC % NW == 0 && NB - 1 <= NW,
@@ -324,8 +323,6 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
 
     __shared__ float Kc[CC][PA];     // the chunk's normalised keys
     __shared__ float QKb[CC * PQB];  // its normalised queries [CC][PA], then diag(beta gamma) K [CC][PB]
-    __shared__ float Gm[CC][PG];     // K K^T (lower triangle of 16 x 16 tiles)
-    __shared__ float Qk[CC][PG];     // Q K^T (same)
     __shared__ float Am[CC][PC];     // A (strictly lower), per v-head
     __shared__ float Tm[CC][PC];     // T = (I + A)^-1
     __shared__ float Vb[CC][PV];     // diag(beta) V, VSL columns
@@ -414,25 +411,24 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
     __syncthreads();
 
     // -- K K^T and Q K^T on the 16 x 16 tiles on and below the diagonal (A and
-    // Aqk are lower triangular), one read of the keys for both
-    {
-        constexpr int NTRI = NB * (NB + 1) / 2;
-        for (int u = wave; u < NTRI; u += NW) {
-            int tm = 0, tn = u;  // u = tm (tm + 1) / 2 + tn, tn <= tm
-            while (tn > tm) {
-                tn -= tm + 1;
-                ++tm;
-            }
-            const int m0 = 16 * tm, n0 = 16 * tn;
-            f32x4 ga, qa;
-            mfma_tile2<DK / 4>([&](int t, int i) { return Kc[t][i]; }, [&](int t, int i) { return Qc(t, i); },
-                               [&](int i, int s2) { return Kc[s2][i]; }, m0, n0, 0, ga, qa);
+    // Aqk are lower triangular), one read of the keys for both; each wave keeps its
+    // tiles (u = wave, wave + NW, ...) in registers for every v-head
+    constexpr int NTRI = NB * (NB + 1) / 2, NTW = (NTRI + NW - 1) / NW;
+    f32x4 gk[NTW], gq2[NTW];
+    int tmw[NTW], tnw[NTW];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                Gm[m0 + 4 * lg + r][n0 + li] = ga[r];
-                Qk[m0 + 4 * lg + r][n0 + li] = qa[r];
-            }
+    for (int k = 0; k < NTW; ++k) {
+        const int u = wave + NW * k;
+        int tm = 0, tn = u;  // u = tm (tm + 1) / 2 + tn, tn <= tm
+        while (tn > tm) {
+            tn -= tm + 1;
+            ++tm;
         }
+        tmw[k] = tm;
+        tnw[k] = tn;
+        if (u < NTRI)
+            mfma_tile2<DK / 4>([&](int t, int i) { return Kc[t][i]; }, [&](int t, int i) { return Qc(t, i); },
+                               [&](int i, int s2) { return Kc[s2][i]; }, 16 * tm, 16 * tn, 0, gk[k], gq2[k]);
     }
 
     constexpr int VPT = CC * VSL / NT;
@@ -489,12 +485,26 @@ __global__ __launch_bounds__(kPrepThreads, 1) __attribute__((amdgpu_waves_per_eu
         // below the diagonal of K K^T and Q K^T were computed: select, not scale.
         {
             float *aq = p.gaq + ((int64_t)chunk * Hv + h) * CC * CC;
+            // the tiles this wave holds: lane (li, lg) has rows 16 tm + 4 lg + r,
+            // column 16 tn + li
+#pragma unroll
+            for (int k = 0; k < NTW; ++k) {
+                if (wave + NW * k < NTRI) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * tmw[k] + 4 * lg + r, s2 = 16 * tnw[k] + li;
+                        const float dg = s2 <= t ? expf(G_s[t] - G_s[s2]) : 0.f;
+                        Am[t][s2] = s2 < t ? beta_s[t] * dg * gk[k][r] : 0.f;
+                        put_pair(aq, CC * CC, t * CC + s2, s2 <= t ? hc.scale * dg * gq2[k][r] : 0.f);
+                    }
+                }
+            }
+            // zeros above the diagonal tiles (A's are never read; Aqk's are)
 #pragma unroll
             for (int i = 0; i < CC * CC / NT; ++i) {
                 const int e = tid + NT * i, t = e / CC, s2 = e % CC;
-                const float dg = s2 <= t ? expf(G_s[t] - G_s[s2]) : 0.f;
-                Am[t][s2] = s2 < t ? beta_s[t] * dg * Gm[t][s2] : 0.f;
-                put_pair(aq, CC * CC, e, s2 <= t ? hc.scale * dg * Qk[t][s2] : 0.f);
+                if (s2 / 16 > t / 16)
+                    put_pair(aq, CC * CC, e, 0.f);
             }
             float *ke = p.gke + ((int64_t)chunk * Hv + h) * CC * DK;
 #pragma unroll
